@@ -1,0 +1,247 @@
+"""ISD step benchmark on one MI355X.
+
+One step = the whole hot path over one batch of 64 requests at stride N=4 (7 query rows
+each), on synthetic inputs already resident in HBM:
+  1. R-ISD gated projection  448 x 4096 -> 4096, rank-128 delta on the 4 [MASK] rows
+  2. attention               Qwen3-8B shapes (32 q / 8 kv heads, D=128), contexts ~ U[512,4096]
+  3. verification            vocab 151936, anchor ~ N(0,3), proposal = anchor + N(0,0.3)
+Prints ONE JSON line: ISD steps/s (value), accepted tokens/s, per-kernel times, the
+attention kernel against the HBM roofline, and the CPU oracle on a bounded sample.
+
+The attention stream (~600 MB) exceeds the 256 MB last-level cache, so every kernel of a
+step starts cold with respect to the previous step's data.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ISD steps/s and accepted tokens/s at N=4, C=64 (1 GPU); % HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--verify-sets", type=int, default=3,
+                    help="distinct seeded verification inputs rotated over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM counters)")
+    return ap.parse_args()
+
+
+def tpf_closed_form(N, p):
+    """Tokens per forward of ISD at acceptance rate p (page 5, "Speedup Factor Explorer")."""
+    return (2 + sum(p ** k for k in range(1, N - 1))) / (2 - p ** (N - 1))
+
+
+def attention_bytes(ctx_lens, R, Hq, Hkv, D, s=2):
+    """Algorithmic bytes of one attention launch: K and V of every token read once
+    (cached tokens and the block), the block's K/V written to the cache, Q read, O written,
+    and the page-table entries used."""
+    L = np.asarray(ctx_lens, np.int64)
+    kv_read = int(np.sum(L + R)) * Hkv * D * 2 * s
+    append = len(L) * R * Hkv * D * 2 * s
+    qo = 2 * len(L) * R * Hq * D * s
+    pages = int(np.sum((L + R + 15) // 16)) * 4
+    return kv_read + append + qo + pages
+
+
+def verify_bytes(B, N, V, n_rejected_sampled, s=2):
+    """Logit rows + draft rows once, the two rows of each rejected request once more,
+    one 1024-entry sub-chunk per sampled row."""
+    R = 2 * N - 1
+    return B * R * V * s + B * (N - 1) * V * s + n_rejected_sampled * 2 * V * s + B * N * 1024 * s
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(requests shard by data parallelism with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from strided_verify_propose_amd import isd, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dt(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    scfg = synth.QWEN3_8B if args.workload == "qwen3_8b" else synth.QWEN3_32B
+    pcfg = synth.PROJ
+    t0 = time.time()
+    # ---- inputs (seeded, generated on the host once, then resident in HBM)
+    att = synth.attention_inputs(scfg)
+    A = dict(q=dt(att.q), k_new=dt(att.k_new), v_new=dt(att.v_new),
+             k_cache=dt(synth.k_tile_layout(att.k_pages)), v_cache=dt(synth.v_tile_layout(att.v_pages)),
+             page_table=dt(att.page_table), ctx_lens=dt(att.ctx_lens))
+    maxctx = int(att.ctx_lens.max())
+    vsets = []
+    for k in range(args.verify_sets):
+        v = synth.verify_inputs(scfg, seed=scfg.seed + 100 * k)
+        vsets.append(dict(logits=dt(v.logits), draft_logits=dt(v.draft_logits),
+                          draft_ids=dt(v.draft_ids), uniforms=dt(v.uniforms)))
+    pin = synth.proj_inputs(pcfg)
+    P = dict(x=dt(pin.x), w=dt(pin.w), a=dt(pin.a), b=dt(pin.b), gate=dt(pin.gate))
+    gen_s = time.time() - t0
+
+    att_out = torch.empty_like(A["q"])
+    y = torch.empty((pcfg.M, pcfg.Nout), dtype=torch.bfloat16, device=dev)
+    vouts = [None] * len(vsets)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        isd.gated_lora_proj(P["x"], P["w"], P["a"], P["b"], P["gate"], out=y)
+        if ev is not None:
+            ev[1].record()
+        isd.attention_step(A["q"], A["k_new"], A["v_new"], A["k_cache"], A["v_cache"],
+                           A["page_table"], A["ctx_lens"], maxctx, out=att_out)
+        if ev is not None:
+            ev[2].record()
+        k = i % len(vsets)
+        vs = vsets[k]
+        vouts[k] = isd.verify(vs["logits"], vs["draft_logits"], vs["draft_ids"], vs["uniforms"],
+                              with_diagnostics=False, out=vouts[k])
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, events around each call on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    proj_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    att_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ver_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # ---- acceptance statistics from the kernel's own outputs
+    n_acc = np.concatenate([vouts[k]["n_accept"].cpu().numpy() for k in range(len(vsets))])
+    N = scfg.N
+    rej = n_acc < N - 1
+    tpf_hat = float((np.mean(n_acc + 1) + rej.mean()) / (1 + rej.mean()))
+    evaluated = np.sum(n_acc + rej)
+    p_hat = float(np.sum(n_acc) / evaluated)
+    steps_per_s = args.steps / elapsed
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    a_bytes = attention_bytes(att.ctx_lens, scfg.R, scfg.Hq, scfg.Hkv, scfg.D)
+    a_us = float(np.mean(att_ms)) * 1e3
+    a_gbps = a_bytes / (a_us * 1e-6) / 1e9
+    v_bytes = verify_bytes(scfg.B, N, scfg.V, int(rej.sum() / len(vsets)))
+    v_us = float(np.mean(ver_ms)) * 1e3
+    m_g = int(pin.gate.sum())
+    p_flops = 2 * pcfg.M * pcfg.K * pcfg.Nout + 2 * m_g * pcfg.K * pcfg.r + 2 * m_g * pcfg.r * pcfg.Nout
+    p_us = float(np.mean(proj_ms)) * 1e3
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"isd_step_{scfg.name}_plus_rlora_proj",
+            "batch": scfg.B, "stride_N": N, "query_rows": scfg.R, "q_heads": scfg.Hq,
+            "kv_heads": scfg.Hkv, "head_dim": scfg.D, "page_size": 16,
+            "context": f"U[{scfg.ctx[1]},{scfg.ctx[2]}]" if scfg.ctx[0] == "uniform" else scfg.ctx[1],
+            "vocab": scfg.V, "proj": f"{pcfg.M}x{pcfg.K}->{pcfg.Nout} r{pcfg.r}",
+            "verify_input_sets": len(vsets),
+        },
+        "accepted_tokens_per_s": round(steps_per_s * scfg.B * tpf_hat, 1),
+        "hot_tokens_per_step": round(float(np.mean(n_acc + 1)) * scfg.B, 2),
+        "tpf_meas": round(tpf_hat, 4),
+        "p_hat": round(p_hat, 4),
+        "tpf_closed_form_at_p_hat": round(tpf_closed_form(N, p_hat), 4),
+        "kernels_us": {"gated_lora_proj": round(p_us, 2), "attention": round(a_us, 2),
+                       "verify": round(v_us, 2)},
+        "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
+        "roofline": {"bound": "hbm", "kernel": "attn_bf16_kernel (isd_attention_step)",
+                     "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": a_bytes},
+        "input_generation_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(scfg, pcfg, att, pin)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(scfg, pcfg, att, pin, att_requests=4, ver_requests=8):
+    """The oracle, as it is, on a bounded sample of the same workload: the full projection,
+    attention for `att_requests` requests and verification for `ver_requests` requests,
+    scaled to one full 64-request step."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from strided_verify_propose_amd import synth
+    t0 = time.perf_counter()
+    oracle.gated_lora_proj(pin.x, pin.w, pin.a, pin.b, pin.gate)
+    t_proj = time.perf_counter() - t0
+    bs = np.arange(att_requests)
+    t0 = time.perf_counter()
+    oracle.attention_step(att.q[bs], att.k_new[bs], att.v_new[bs], att.k_pages, att.v_pages,
+                          att.page_table[bs], att.ctx_lens[bs], att.scale)
+    t_att = (time.perf_counter() - t0) * float(np.sum(att.ctx_lens + scfg.R)) / \
+        float(np.sum(att.ctx_lens[bs] + scfg.R))
+    vc = synth.StepConfig(scfg.name, scfg.dtype, B=ver_requests, N=scfg.N, Hq=scfg.Hq,
+                          Hkv=scfg.Hkv, D=scfg.D, V=scfg.V, ctx=scfg.ctx, anchor_sd=scfg.anchor_sd,
+                          noise_sd=scfg.noise_sd, seed=scfg.seed)
+    v = synth.verify_inputs(vc)
+    t0 = time.perf_counter()
+    oracle.verify_step(v.logits, v.draft_logits, v.draft_ids, v.uniforms, scfg.N)
+    t_ver = (time.perf_counter() - t0) * scfg.B / ver_requests
+    step_s = t_proj + t_att + t_ver
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"full projection, attention for {att_requests} of {scfg.B} requests "
+                       f"(scaled by tokens), verification for {ver_requests} of {scfg.B} "
+                       f"requests (scaled by count); one step = {step_s:.1f} s"),
+            "seconds": {"proj": round(t_proj, 2), "attention_scaled": round(t_att, 2),
+                        "verify_scaled": round(t_ver, 2)}}
+
+
+if __name__ == "__main__":
+    main()

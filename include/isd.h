@@ -1,0 +1,156 @@
+/* isd.h -- C ABI of the MI355X (gfx950) hot path of Introspective Strided Decoding.
+ *
+ * One ISD decode step runs a block of 2N-1 query rows per request: N-1 rows verify the
+ * previous step's proposals against the causal anchor distribution p, N [MASK] rows
+ * propose new tokens (page 1 "I-DLM 如何解決這些問題"; page 3 "1. 引言"; page 5
+ * "Inference & ISD").  The library provides the three data-parallel parts of that step:
+ *
+ *   isd_attention_step   strictly causal GQA attention of the block over a paged KV cache
+ *   isd_verify           vocab-wide p/q verification, residual resampling, argmax proposals
+ *   isd_gated_lora_proj  R-ISD projection: base weights on every row, LoRA delta on gated rows
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers, dense and row-major in the shapes given, owned
+ *     by the caller.  The library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream).  Nothing is synchronised; outputs are ready when the stream is.
+ *   - Shapes, dtypes and pointers are checked on the host before anything is launched.
+ *     A failed check returns ISD_ERR_INVALID_ARG (bad value), ISD_ERR_UNSUPPORTED (valid
+ *     but outside what the kernels implement) or ISD_ERR_WORKSPACE (too small), and
+ *     launches nothing.  A failed launch returns ISD_ERR_HIP.  isd_last_error() then
+ *     holds a message for the calling thread.
+ *   - Values stored on the device (context lengths, page ids, draft ids) are
+ *     preconditions and are not range-checked there.  Inputs must be finite.
+ *   - Results are bitwise reproducible for the same inputs and shapes (fixed reduction
+ *     orders, no floating-point atomics).
+ *   - Each entry point has its own workspace (device memory, caller-owned, at least the
+ *     size its *_workspace_bytes query returns).  It must be ZERO-FILLED before its first
+ *     use with a given set of shape arguments (where the completion counters sit depends
+ *     on the shapes); every call that completes leaves its counters at zero again, so a
+ *     workspace can be reused for the same shapes without clearing.  Calls that share a
+ *     workspace must not run concurrently.
+ *   - bf16 values are IEEE binary32 truncated to their upper 16 bits (uint16 storage).
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISD_ABI_VERSION 1
+#define ISD_PAGE_SIZE 16
+
+typedef enum {
+  ISD_OK = 0,
+  ISD_ERR_INVALID_ARG = 1,
+  ISD_ERR_UNSUPPORTED = 2,
+  ISD_ERR_WORKSPACE = 3,
+  ISD_ERR_HIP = 4
+} isd_status;
+
+typedef enum { ISD_F32 = 0, ISD_BF16 = 1 } isd_dtype;
+
+int isd_abi_version(void);
+const char* isd_status_string(isd_status s);
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* isd_last_error(void);
+
+/* ---------------------------------------------------------------- attention
+ * Strictly causal GQA attention of the 2N-1 block rows over a paged KV cache.
+ * Follows: the block of 2N-1 query positions per forward (page 1, section
+ * "為什麼 I-DLM 能在高並發下保持高效"); strictly causal attention, which keeps the model
+ * on an AR serving stack (page 1 "實際部署：SGLang 整合"; page 5 "I-DLM-Methodik"); a
+ * paged KV cache read only through its pages (page 1 "實際部署：SGLang 整合"; page 5
+ * "Serving (SGLang)").
+ *
+ * R = 2N-1, G = Hq/Hkv.  dtype ISD_BF16 or ISD_F32 for every tensor.
+ *   q, out        [B, R, Hq, D]      query rows of the block, attention output
+ *   k_new, v_new  [B, R, Hkv, D]     the block's keys/values (after any positional transform)
+ *   k_cache       [num_pages, Hkv, D/8, 16, 8]      per page and KV head: blocks of 8 dims,
+ *                 16 token slots each -- element (page p, head h, slot t, dim d) sits at
+ *                 ((p*Hkv + h)*(D/8) + d/8)*128 + t*8 + d%8
+ *   v_cache       [num_pages, Hkv, D/16, 4, 16, 4]  element (p, h, t, d) sits at
+ *                 ((p*Hkv + h)*(D/16) + d/16)*256 + (t/4)*64 + (d%16)*4 + t%4
+ *   page_table    [B, max_pages_per_seq] int32: physical page of logical page j of request b
+ *   ctx_lens      [B] int32: tokens cached BEFORE this block (device array)
+ * Effect: block row r of request b is written to token slot ctx_lens[b] + r (a bit copy;
+ *   no other slot changes), and
+ *   out[b,r,h] = sum_j softmax_j(scale * q[b,r,h].k_j) v_j  over tokens j = 0..ctx_lens[b]+r,
+ *   KV head h / G.  The block's own keys are used as written, so the result equals attention
+ *   read entirely through the pages after the append.  Rejected tokens are rolled back by the
+ *   caller simply not advancing ctx_lens; their slots are overwritten by the next step.
+ * Requires: page_size == 16, D in {64, 128}, Hq % Hkv == 0, R*G <= 64 (bf16) / any (f32),
+ *   every page the request touches (ctx_lens[b]+R tokens) present in its page table,
+ *   0 <= ctx_lens[b] <= max_ctx_len, max_ctx_len + R <= 16*max_pages_per_seq;
+ *   for ISD_F32 also max_ctx_len + R <= 16384.
+ * scale: usually 1/sqrt(D). */
+size_t isd_attention_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_ctx_len);
+isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const int32_t* page_table,
+                              const int32_t* ctx_lens, void* out, int B, int N, int Hq, int Hkv,
+                              int D, int page_size, int max_pages_per_seq, int num_pages,
+                              int max_ctx_len, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- verification
+ * Vocab-wide verification of one ISD step.  Follows: proposals at [MASK] positions from
+ * q and verification at clean positions against the anchor p with acceptance
+ * min(1, p(x)/q(x)), which keeps the output distribution that of the AR model (page 1
+ * "I-DLM 如何解決這些問題"; page 5 "Inference & ISD"); argmax proposals (page 1
+ * "實際部署：SGLang 整合"; page 5 "Serving (SGLang)").  On a rejection the next token is
+ * drawn from the normalised residual max(0, p - q~), the completion that keeps that
+ * guarantee (the pages do not print it).
+ *
+ * Rows per request (R = 2N-1): logits rows 0..N-2 are the anchors p_i verifying draft
+ * d_i = draft_ids[b][i]; rows N-1..2N-2 are the proposal rows.  Every row is softmax(l/T).
+ *   logits        [B, R, V]      dtype dt
+ *   draft_logits  [B, N-1, V]    row i is q~_i, the distribution d_i was drawn from (the
+ *                 previous step's proposal row); NULL => argmax drafts: q~_i is one-hot on
+ *                 d_i, so a_i = p_i(d_i) and the residual is p_i with d_i removed
+ *   draft_ids     [B, N-1] int32 in [0, V)
+ *   uniforms      [B, R] float in [0, 1): u[b][i] for draft i's test (reused as
+ *                 (u - a)/(1 - a) for the residual draw), u[b][N-1+j] for proposal row j
+ * Walk: a_i = 1 if P >= Q else P/Q with P = p_i(d_i), Q = q~_i(d_i); accept iff u < a_i;
+ * stop at the first rejection.  Inverse CDF = smallest id k with cumulative mass > u.
+ * Outputs (all written for every request):
+ *   n_accept      [B] int32 in 0..N-1
+ *   accept        [B, N-1] uint8, 0 after the first rejection
+ *   next_token    [B] int32: residual draw if n_accept < N-1, else sampled_ids[b][0]
+ *   argmax_ids    [B, N] int32: argmax of each proposal row over the raw logits, lowest id on ties
+ *   sampled_ids   [B, N] int32: inverse-CDF draw of proposal row j at u[b][N-1+j]
+ * Optional outputs (NULL to skip):
+ *   p_draft, q_draft [B, N-1] float: P and Q of every draft (Q = 1 for argmax drafts)
+ *   row_lse       [B, R + N-1] float: log-sum-exp of l/T per logits row, then per draft row
+ *                 (0 for draft rows when draft_logits is NULL)
+ * Requires: 1 <= N <= 8, V >= 2, temperature > 0.  Not written on error. */
+size_t isd_verify_workspace_bytes(int B, int N, int V);
+isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits,
+                      const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                      float temperature, int32_t* n_accept, uint8_t* accept,
+                      int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                      float* p_draft, float* q_draft, float* row_lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- R-ISD projection
+ * Gated residual adaptation of one linear layer: the LoRA delta is applied only on gated
+ * ([MASK]) rows and verify rows use the base weights alone, so they equal the base model's
+ * output bit for bit (page 1 "無損 R-ISD"; page 3 "1. 引言"; page 5 "Lossless R-ISD").
+ * bf16 only; fp32 accumulation.  Storage follows the linear-layer convention:
+ *   x [M, K]; w [Nout, K] (= W^T); a [r, K] (= A^T); b [Nout, r] (= B^T); y [M, Nout]
+ *   gate [M] uint8 in {0, 1}; NULL => base-only (a and b may then be NULL)
+ * Computes y = x W + gate * (bf16(x A)) B, rounded to bf16.  Rows with gate 0 are
+ * bit-identical to the base-only call on the same x, w.
+ * Requires: K % 64 == 0, Nout % 128 == 0, r in {128, 256} when gated, 1 <= M <= 65536. */
+size_t isd_gated_lora_workspace_bytes(int M, int K, int Nout, int r);
+isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, const void* b,
+                               const uint8_t* gate, void* y, int M, int K, int Nout, int r,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ISD_H */

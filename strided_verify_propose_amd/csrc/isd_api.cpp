@@ -1,0 +1,286 @@
+// C ABI of the ISD hot path: argument validation (host only, before any launch),
+// workspace layout, and the launches.  See include/isd.h for the contract.
+#include "isd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+isd_status fail(isd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+isd_status ok() {
+  g_err.clear();
+  return ISD_OK;
+}
+
+isd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ISD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- attention workspace
+struct AttnWs {
+  int pps, splits_max;
+  size_t counters, part_o, part_ml, total;
+};
+
+AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
+  AttnWs w{};
+  const int R = 2 * N - 1, G = Hq / Hkv, RG = R * G;
+  const int ncp = (max_ctx_len + ISD_PAGE_SIZE - 1) / ISD_PAGE_SIZE;
+  w.pps = isd::attention_pages_per_split(B, Hkv, max_ctx_len, R);
+  w.splits_max = ncp == 0 ? 1 : (ncp + w.pps - 1) / w.pps;
+  const size_t slots = (size_t)B * Hkv * w.splits_max;
+  w.counters = 0;
+  w.part_o = align256((size_t)B * Hkv * sizeof(uint32_t));
+  w.part_ml = w.part_o + align256(slots * RG * D * sizeof(float));
+  w.total = w.part_ml + align256(slots * RG * 2 * sizeof(float));
+  return w;
+}
+
+// ---------------------------------------------------------------- verify workspace
+struct VerWs {
+  int RR, SV, NSUB;
+  size_t cmax, cidx, csub, ws, rsub, total;
+};
+
+VerWs ver_ws(int B, int N, int V) {
+  VerWs w{};
+  w.RR = (2 * N - 1) + (N - 1);
+  w.SV = (V + isd::VCHUNK - 1) / isd::VCHUNK;
+  w.NSUB = (V + isd::VSUB - 1) / isd::VSUB;
+  const size_t rows = (size_t)B * w.RR;
+  w.cmax = 0;
+  w.cidx = w.cmax + align256(rows * w.SV * sizeof(float));
+  w.csub = w.cidx + align256(rows * w.SV * sizeof(int32_t));
+  w.ws = w.csub + align256(rows * w.NSUB * sizeof(float));
+  w.rsub = w.ws + align256((size_t)B * sizeof(isd::WalkState));
+  w.total = w.rsub + align256((size_t)B * w.NSUB * sizeof(float));
+  return w;
+}
+
+// ---------------------------------------------------------------- projection workspace
+int gemm_splits(int M, int N, int K) {
+  const int kb = K / isd::GEMM_BK;
+  if (const char* e = getenv("ISD_GEMM_SPLITS")) {
+    const int s = atoi(e);
+    if (s >= 1 && kb % s == 0) return s;
+  }
+  const long tiles = (long)((M + isd::GEMM_BM - 1) / isd::GEMM_BM) * (N / isd::GEMM_BN);
+  int s = 1;
+  while (tiles * s < 256 && s < 16 && kb % (2 * s) == 0 && kb / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
+struct ProjWs {
+  int s_main, s_down;
+  size_t T, part, cnt_main, cnt_down, total;
+};
+
+ProjWs proj_ws(int M, int K, int Nout, int r) {
+  ProjWs w{};
+  w.s_main = gemm_splits(M, Nout, K);
+  w.s_down = r > 0 ? gemm_splits(M, r, K) : 1;
+  const size_t tm = (M + isd::GEMM_BM - 1) / isd::GEMM_BM;
+  const size_t part_main = w.s_main > 1 ? (size_t)w.s_main * M * Nout : 0;
+  const size_t part_down = (r > 0 && w.s_down > 1) ? (size_t)w.s_down * M * r : 0;
+  w.cnt_main = 0;
+  w.cnt_down = align256(tm * (Nout / isd::GEMM_BN) * sizeof(uint32_t));
+  w.T = w.cnt_down + align256(tm * (r > 0 ? (size_t)(r / isd::GEMM_BN) : 1) * sizeof(uint32_t));
+  w.part = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
+  w.total = w.part + align256((part_main > part_down ? part_main : part_down) * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int isd_abi_version(void) { return ISD_ABI_VERSION; }
+
+const char* isd_status_string(isd_status s) {
+  switch (s) {
+    case ISD_OK: return "ok";
+    case ISD_ERR_INVALID_ARG: return "invalid argument";
+    case ISD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ISD_ERR_WORKSPACE: return "workspace too small";
+    case ISD_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* isd_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------- attention
+size_t isd_attention_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_ctx_len < 0) return 0;
+  return attn_ws(B, N, Hq, Hkv, D, max_ctx_len).total;
+}
+
+isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const int32_t* page_table,
+                              const int32_t* ctx_lens, void* out, int B, int N, int Hq, int Hkv,
+                              int D, int page_size, int max_pages_per_seq, int num_pages,
+                              int max_ctx_len, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dt != ISD_F32 && dt != ISD_BF16) return fail(ISD_ERR_INVALID_ARG, "attention: unknown dtype %d", (int)dt);
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !page_table || !ctx_lens || !out)
+    return fail(ISD_ERR_INVALID_ARG, "attention: null tensor pointer");
+  if (B < 1 || B > 65535) return fail(ISD_ERR_INVALID_ARG, "attention: B=%d out of [1, 65535]", B);
+  if (N < 1 || N > 64) return fail(ISD_ERR_INVALID_ARG, "attention: N=%d out of [1, 64]", N);
+  if (Hq < 1 || Hkv < 1 || Hkv > 65535 || Hq % Hkv)
+    return fail(ISD_ERR_INVALID_ARG, "attention: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(ISD_ERR_UNSUPPORTED, "attention: D=%d (supported: 64, 128)", D);
+  if (page_size != ISD_PAGE_SIZE)
+    return fail(ISD_ERR_UNSUPPORTED, "attention: page_size=%d (supported: 16)", page_size);
+  if (max_pages_per_seq < 1 || num_pages < 1)
+    return fail(ISD_ERR_INVALID_ARG, "attention: max_pages_per_seq=%d num_pages=%d", max_pages_per_seq, num_pages);
+  const int R = 2 * N - 1, G = Hq / Hkv;
+  if (max_ctx_len < 0 || (long)max_ctx_len + R > (long)ISD_PAGE_SIZE * max_pages_per_seq)
+    return fail(ISD_ERR_INVALID_ARG, "attention: max_ctx_len=%d + %d block rows exceeds %d pages", max_ctx_len, R, max_pages_per_seq);
+  if (!std::isfinite(scale)) return fail(ISD_ERR_INVALID_ARG, "attention: scale is not finite");
+  if (dt == ISD_BF16 && R * G > 64)
+    return fail(ISD_ERR_UNSUPPORTED, "attention: (2N-1)*Hq/Hkv = %d query rows per KV head (max 64)", R * G);
+  if (dt == ISD_F32 && max_ctx_len + R > 16384)
+    return fail(ISD_ERR_UNSUPPORTED, "attention: f32 path holds at most 16384 tokens");
+  const AttnWs w = attn_ws(B, N, Hq, Hkv, D, max_ctx_len);
+  if (dt == ISD_BF16 && (!workspace || workspace_bytes < w.total))
+    return fail(ISD_ERR_WORKSPACE, "attention: workspace %zu bytes, need %zu", workspace_bytes, w.total);
+
+  isd::AttnLaunch a{};
+  a.dtype = dt == ISD_BF16 ? 1 : 0;
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.page_table = page_table; a.ctx_lens = ctx_lens; a.out = out;
+  a.B = B; a.N = N; a.R = R; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.D = D;
+  a.max_pages = max_pages_per_seq; a.num_pages = num_pages; a.max_ctx_len = max_ctx_len; a.scale = scale;
+  a.pages_per_split = w.pps; a.splits_max = w.splits_max;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = ws ? reinterpret_cast<uint32_t*>(ws + w.counters) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(ws + w.part_o) : nullptr;
+  a.part_ml = ws ? reinterpret_cast<float*>(ws + w.part_ml) : nullptr;
+  return hip_status(isd::launch_attention(a, static_cast<hipStream_t>(stream)), "attention launch");
+}
+
+// ---------------------------------------------------------------- verification
+size_t isd_verify_workspace_bytes(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 2) return 0;
+  return ver_ws(B, N, V).total;
+}
+
+isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits,
+                      const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                      float temperature, int32_t* n_accept, uint8_t* accept,
+                      int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                      float* p_draft, float* q_draft, float* row_lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (dt != ISD_F32 && dt != ISD_BF16) return fail(ISD_ERR_INVALID_ARG, "verify: unknown dtype %d", (int)dt);
+  if (B < 1 || B > 65535) return fail(ISD_ERR_INVALID_ARG, "verify: B=%d out of [1, 65535]", B);
+  if (N < 1 || N > 8) return fail(ISD_ERR_UNSUPPORTED, "verify: N=%d (supported: 1..8)", N);
+  if (V < 2 || V > (1 << 20)) return fail(ISD_ERR_UNSUPPORTED, "verify: V=%d (supported: 2..2^20)", V);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(ISD_ERR_INVALID_ARG, "verify: temperature must be finite and > 0");
+  if (!logits || !uniforms || !n_accept || !next_token || !argmax_ids || !sampled_ids)
+    return fail(ISD_ERR_INVALID_ARG, "verify: null tensor pointer");
+  if (N > 1 && (!draft_ids || !accept))
+    return fail(ISD_ERR_INVALID_ARG, "verify: draft_ids and accept are required when N > 1");
+  const VerWs w = ver_ws(B, N, V);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(ISD_ERR_WORKSPACE, "verify: workspace %zu bytes, need %zu", workspace_bytes, w.total);
+
+  isd::VerifyLaunch v{};
+  v.dtype = dt == ISD_BF16 ? 1 : 0;
+  v.logits = logits;
+  v.draft = (N > 1) ? draft_logits : nullptr;
+  v.draft_ids = draft_ids; v.u = uniforms;
+  v.B = B; v.N = N; v.R = 2 * N - 1;
+  v.RR = v.R + (v.draft ? N - 1 : 0);
+  v.V = V; v.SV = w.SV; v.NSUB = w.NSUB;
+  v.invT = 1.f / temperature;
+  v.c2 = (float)(1.4426950408889634 / (double)temperature);
+  v.n_accept = n_accept; v.accept = accept; v.next_token = next_token;
+  v.argmax_ids = argmax_ids; v.sampled_ids = sampled_ids;
+  v.p_draft = p_draft; v.q_draft = q_draft; v.row_lse = row_lse;
+  char* ws = static_cast<char*>(workspace);
+  v.cmax = reinterpret_cast<float*>(ws + w.cmax);
+  v.cidx = reinterpret_cast<int32_t*>(ws + w.cidx);
+  v.csub = reinterpret_cast<float*>(ws + w.csub);
+  v.ws = reinterpret_cast<isd::WalkState*>(ws + w.ws);
+  v.rsub = reinterpret_cast<float*>(ws + w.rsub);
+  return hip_status(isd::launch_verify(v, static_cast<hipStream_t>(stream)), "verify launch");
+}
+
+// ---------------------------------------------------------------- gated projection
+size_t isd_gated_lora_workspace_bytes(int M, int K, int Nout, int r) {
+  if (M < 1 || K < 64 || K % 64 || Nout < 128 || Nout % 128 || r < 0) return 0;
+  return proj_ws(M, K, Nout, r).total;
+}
+
+isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, const void* b,
+                               const uint8_t* gate, void* y, int M, int K, int Nout, int r,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w || !y) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj: null tensor pointer");
+  if (M < 1 || M > 65536) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj: M=%d out of [1, 65536]", M);
+  if (K < 64 || K % 64) return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj: K=%d (multiple of 64 required)", K);
+  if (Nout < 128 || Nout % 128)
+    return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj: Nout=%d (multiple of 128 required)", Nout);
+  const bool lora = gate != nullptr;
+  if (lora) {
+    if (!a || !b) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj: gate given without a, b");
+    if (r != 128 && r != 256)
+      return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj: r=%d (supported: 128, 256)", r);
+  }
+  const ProjWs ws_ = proj_ws(M, K, Nout, lora ? r : 0);
+  if (!workspace || workspace_bytes < ws_.total)
+    return fail(ISD_ERR_WORKSPACE, "gated_lora_proj: workspace %zu bytes, need %zu", workspace_bytes, ws_.total);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* T = reinterpret_cast<uint16_t*>(ws + ws_.T);
+  float* part = reinterpret_cast<float*>(ws + ws_.part);
+  if (lora) {
+    isd::GemmLaunch d{};
+    d.A = static_cast<const uint16_t*>(x);
+    d.B = static_cast<const uint16_t*>(a);
+    d.M = M; d.N = r; d.K = K; d.splits = ws_.s_down;
+    d.part = part;
+    d.counters = reinterpret_cast<uint32_t*>(ws + ws_.cnt_down);
+    d.C = T;
+    hipError_t e = isd::launch_gemm(d, s);
+    if (e != hipSuccess) return hip_status(e, "gated_lora_proj down-projection launch");
+  }
+  isd::GemmLaunch g{};
+  g.A = static_cast<const uint16_t*>(x);
+  g.B = static_cast<const uint16_t*>(w);
+  g.M = M; g.N = Nout; g.K = K; g.splits = ws_.s_main;
+  g.part = part;
+  g.counters = reinterpret_cast<uint32_t*>(ws + ws_.cnt_main);
+  g.C = static_cast<uint16_t*>(y);
+  if (lora) {
+    g.T = T;
+    g.Bl = static_cast<const uint16_t*>(b);
+    g.gate = gate;
+    g.r = r;
+  }
+  return hip_status(isd::launch_gemm(g, s), "gated_lora_proj launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Host-side launch interface between the C ABI (isd_api.cpp) and the kernels (*.hip).
+// Arguments have already been validated when these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace isd {
+
+// ---------------------------------------------------------------- attention
+struct AttnLaunch {
+  int dtype;  // 0 f32, 1 bf16
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  void* out;
+  int B, N, R, Hq, Hkv, G, D;
+  int max_pages;
+  int num_pages;
+  int max_ctx_len;
+  float scale;
+  int pages_per_split;   // cached pages handled by one workgroup (multiple of 4)
+  int splits_max;        // grid extent over splits
+  // workspace carve-up
+  uint32_t* counters;    // [B*Hkv], zero between calls
+  float* part_o;         // [B*Hkv*splits_max][R*G][D]
+  float* part_ml;        // [B*Hkv*splits_max][R*G][2]
+};
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+int attention_pages_per_split(int B, int Hkv, int max_ctx_len, int R);
+
+// ---------------------------------------------------------------- verification
+constexpr int VCHUNK = 16384;   // vocab entries per stats workgroup
+constexpr int VSUB = 1024;      // vocab entries per sub-chunk (prefix granularity)
+constexpr int VCHUNK_SUBS = VCHUNK / VSUB;
+
+struct WalkState {              // per request, written by the walk, read by the residual pass
+  int rej;                      // first rejected draft index, -1 if none / handled in the walk
+  int pad;
+  double up;                    // (u - a) / (1 - a)
+  float mp, mq;                 // row maxima (raw logits) of p_{rej} and q~_{rej}
+  float izp_hi, izp_lo;         // 1/Z of p_{rej} in units of 2^((l - mp) * c2), split hi + lo
+  float izq_hi, izq_lo;
+};
+
+struct VerifyLaunch {
+  int dtype;
+  const void* logits;
+  const void* draft;            // may be null
+  const int32_t* draft_ids;
+  const float* u;
+  int B, N, R, RR, V, SV, NSUB;
+  float invT, c2;               // 1/T and log2(e)/T
+  int32_t* n_accept;
+  uint8_t* accept;
+  int32_t* next_token;
+  int32_t* argmax_ids;
+  int32_t* sampled_ids;
+  float* p_draft;
+  float* q_draft;
+  float* row_lse;
+  // workspace
+  float* cmax;                  // [B][RR][SV]  chunk max of raw logits
+  int32_t* cidx;                // [B][RR][SV]  lowest index of the chunk max
+  float* csub;                  // [B][RR][NSUB] sum 2^((l - cmax)*c2) per sub-chunk
+  WalkState* ws;                // [B]
+  float* rsub;                  // [B][NSUB] residual mass per sub-chunk
+};
+hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);
+
+// ---------------------------------------------------------------- gated projection
+struct GemmLaunch {
+  const uint16_t* A;            // [M, K]
+  const uint16_t* B;            // [N, K]
+  int M, N, K;
+  int splits;                   // split-K factor (K/splits multiple of 64)
+  float* part;                  // [splits][M][N] fp32 (splits > 1)
+  uint32_t* counters;           // [tiles_m * tiles_n] (splits > 1)
+  uint16_t* C;                  // [M, N] bf16 output
+  // optional LoRA epilogue: C += gate ? T * Bl^T : 0
+  const uint16_t* T;            // [M, r] bf16
+  const uint16_t* Bl;           // [N, r]
+  const uint8_t* gate;          // [M]
+  int r;
+};
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+constexpr int GEMM_BM = 128, GEMM_BN = 128, GEMM_BK = 64;
+
+}  // namespace isd

@@ -1,0 +1,214 @@
+"""Python binding of libisd.so (the C ABI in include/isd.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and layout,
+their data pointers and the current HIP stream are passed through ctypes, and every
+step of the computation runs in the library's kernels.  PyTorch provides device
+memory and streams.  There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisd.so")
+_lib = None
+
+ISD_F32, ISD_BF16 = 0, 1
+PAGE_SIZE = 16
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace too small", 4: "HIP error"}
+
+EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
+           "isd_attention_workspace_bytes", "isd_attention_step",
+           "isd_verify_workspace_bytes", "isd_verify",
+           "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj")
+
+
+class IsdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Open the library (after torch, so it binds to the HIP runtime torch loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m strided_verify_propose_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.isd_abi_version.restype = i32
+    L.isd_status_string.restype = ctypes.c_char_p
+    L.isd_status_string.argtypes = [i32]
+    L.isd_last_error.restype = ctypes.c_char_p
+    L.isd_attention_workspace_bytes.restype = sz
+    L.isd_attention_workspace_bytes.argtypes = [i32] * 6
+    L.isd_attention_step.restype = i32
+    L.isd_attention_step.argtypes = [i32] + [vp] * 8 + [i32] * 9 + [f32, vp, sz, vp]
+    L.isd_verify_workspace_bytes.restype = sz
+    L.isd_verify_workspace_bytes.argtypes = [i32] * 3
+    L.isd_verify.restype = i32
+    L.isd_verify.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 8 + [vp, sz, vp]
+    L.isd_gated_lora_workspace_bytes.restype = sz
+    L.isd_gated_lora_workspace_bytes.argtypes = [i32] * 4
+    L.isd_gated_lora_proj.restype = i32
+    L.isd_gated_lora_proj.argtypes = [vp] * 6 + [i32] * 4 + [vp, sz, vp]
+    if L.isd_abi_version() != 1:
+        raise RuntimeError("libisd.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise IsdError(status, lib().isd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must live on the GPU ({device})")
+
+
+_ws_cache: dict = {}
+
+
+def workspace(kind: str, nbytes: int, device, shape_key=()) -> torch.Tensor:
+    """Zero-filled device workspace, one per (entry point, device, shape arguments): the
+    library's completion counters return to zero after each call, but where they sit
+    depends on the shapes."""
+    key = (kind, str(device), tuple(shape_key))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return ISD_BF16
+    if t.dtype == torch.float32:
+        return ISD_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------------------- attention
+def attention_step(q, k_new, v_new, k_cache, v_cache, page_table, ctx_lens, max_ctx_len: int,
+                   out=None, scale: float | None = None, ws=None):
+    """Strictly causal GQA attention of the 2N-1 block rows over the paged cache; appends the
+    block's K/V rows to their slots.  q [B,R,Hq,D]; k_new, v_new [B,R,Hkv,D];
+    k_cache [P,Hkv,D/8,16,8], v_cache [P,Hkv,D/16,4,16,4]; page_table [B,maxp] int32;
+    ctx_lens [B] int32 (device); max_ctx_len: host bound on ctx_lens."""
+    B, R, Hq, D = q.shape
+    if R % 2 == 0:
+        raise ValueError("q must hold 2N-1 rows per request")
+    N = (R + 1) // 2
+    Hkv = k_new.shape[2]
+    dev = q.device
+    _need(q, "q", q.dtype, device=dev)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name, q.dtype, (B, R, Hkv, D), dev)
+    P = k_cache.shape[0]
+    _need(k_cache, "k_cache", q.dtype, (P, Hkv, D // 8, PAGE_SIZE, 8), dev)
+    _need(v_cache, "v_cache", q.dtype, (P, Hkv, D // 16, 4, PAGE_SIZE, 4), dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (B,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L = lib()
+    nbytes = L.isd_attention_workspace_bytes(B, N, Hq, Hkv, D, int(max_ctx_len))
+    w = ws if ws is not None else workspace("attention", nbytes, dev, (B, N, Hq, Hkv, D, int(max_ctx_len)))
+    _check(L.isd_attention_step(_dt(q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(page_table), _ptr(ctx_lens), _ptr(out),
+                                B, N, Hq, Hkv, D, PAGE_SIZE, page_table.shape[1], P,
+                                int(max_ctx_len), float(scale), _ptr(w), w.numel(), _stream(dev)))
+    return out
+
+
+# ----------------------------------------------------------------------------- verification
+def verify(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
+           with_diagnostics: bool = True, out: dict | None = None):
+    """Vocab-wide verification of one ISD step.  logits [B,2N-1,V]; draft_logits [B,N-1,V]
+    or None (argmax drafts); draft_ids [B,N-1] int32; uniforms [B,2N-1] float32.
+    Returns a dict of device tensors (n_accept, accept, next_token, argmax_ids,
+    sampled_ids, and p_draft, q_draft, row_lse when with_diagnostics)."""
+    B, R, V = logits.shape
+    if R % 2 == 0:
+        raise ValueError("logits must hold 2N-1 rows per request")
+    N = (R + 1) // 2
+    dev = logits.device
+    _need(logits, "logits", logits.dtype, device=dev)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", logits.dtype, (B, N - 1, V), dev)
+    _need(draft_ids, "draft_ids", torch.int32, (B, N - 1), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, R), dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(n_accept=torch.empty(B, **i32),
+                   accept=torch.empty((B, N - 1), dtype=torch.uint8, device=dev),
+                   next_token=torch.empty(B, **i32), argmax_ids=torch.empty((B, N), **i32),
+                   sampled_ids=torch.empty((B, N), **i32))
+        if with_diagnostics:
+            f32 = dict(dtype=torch.float32, device=dev)
+            out.update(p_draft=torch.empty((B, N - 1), **f32), q_draft=torch.empty((B, N - 1), **f32),
+                       row_lse=torch.empty((B, R + N - 1), **f32))
+    L = lib()
+    nbytes = L.isd_verify_workspace_bytes(B, N, V)
+    w = workspace("verify", nbytes, dev, (B, N, V))
+    _check(L.isd_verify(_dt(logits), _ptr(logits), _ptr(draft_logits), _ptr(draft_ids),
+                        _ptr(uniforms), B, N, V, float(temperature), _ptr(out["n_accept"]),
+                        _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
+                        _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+                        _ptr(out.get("row_lse")), _ptr(w), w.numel(), _stream(dev)))
+    return out
+
+
+# ----------------------------------------------------------------------------- projection
+def gated_lora_proj(x, w, a=None, b=None, gate=None, out=None):
+    """R-ISD projection y = x W + gate * bf16(x A) B (bf16).  x [M,K]; w [Nout,K] (= W^T);
+    a [r,K] (= A^T); b [Nout,r] (= B^T); gate [M] uint8 or None (base only)."""
+    M, K = x.shape
+    Nout = w.shape[0]
+    dev = x.device
+    bf = torch.bfloat16
+    _need(x, "x", bf, device=dev)
+    _need(w, "w", bf, (Nout, K), dev)
+    r = 0
+    if gate is not None:
+        r = a.shape[0]
+        _need(a, "a", bf, (r, K), dev)
+        _need(b, "b", bf, (Nout, r), dev)
+        _need(gate, "gate", torch.uint8, (M,), dev)
+    if out is None:
+        out = torch.empty((M, Nout), dtype=bf, device=dev)
+    _need(out, "out", bf, (M, Nout), dev)
+    L = lib()
+    nbytes = L.isd_gated_lora_workspace_bytes(M, K, Nout, r)
+    ws = workspace("proj", nbytes, dev, (M, K, Nout, r))
+    _check(L.isd_gated_lora_proj(_ptr(x), _ptr(w), _ptr(a), _ptr(b), _ptr(gate), _ptr(out),
+                                 M, K, Nout, r, _ptr(ws), ws.numel(), _stream(dev)))
+    return out

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports what include/isd.h declares, and host
+validation rejects bad arguments with the documented status before anything is launched.
+(No call here reaches a kernel: every one fails validation first.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from strided_verify_propose_amd import isd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isd.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails before any launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(isd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return isd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 9
+    assert sorted(isd.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.isd_abi_version() == 1
+    assert L.isd_status_string(0) == b"ok"
+    assert L.isd_status_string(3) == b"workspace too small"
+
+
+def att(L, **kw):
+    a = dict(dt=1, B=2, N=4, Hq=32, Hkv=8, D=128, page=16, maxp=10, P=20, maxctx=100,
+             scale=0.088, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    ptrs = [None if kw.get("null_at") == i else FAKE for i in range(8)]
+    return L.isd_attention_step(a["dt"], *ptrs, a["B"], a["N"], a["Hq"], a["Hkv"], a["D"],
+                                a["page"], a["maxp"], a["P"], a["maxctx"], a["scale"],
+                                a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), INVALID),
+    (dict(null_at=0), INVALID),
+    (dict(null_at=6), INVALID),
+    (dict(B=0), INVALID),
+    (dict(Hq=30), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(page=32), UNSUPPORTED),
+    (dict(maxctx=160), INVALID),           # 160 + 7 > 10 pages * 16
+    (dict(maxctx=-1), INVALID),
+    (dict(N=10, Hq=32, Hkv=4, maxp=100), UNSUPPORTED),   # 19 rows * 8 heads > 64
+    (dict(scale=float("inf")), INVALID),
+    (dict(wsb=100), WORKSPACE),
+    (dict(ws=None), WORKSPACE),
+    (dict(dt=0, maxctx=20000, maxp=2000), UNSUPPORTED),  # f32 path token limit
+])
+def test_attention_validation(L, kw, status):
+    assert att(L, **kw) == status
+    assert L.isd_last_error() != b""
+
+
+def ver(L, **kw):
+    a = dict(dt=1, B=4, N=4, V=151936, T=1.0, ws=FAKE, wsb=1 << 30, draft=FAKE, ids=FAKE, acc=FAKE)
+    a.update(kw)
+    return L.isd_verify(a["dt"], FAKE, a["draft"], a["ids"], FAKE, a["B"], a["N"], a["V"],
+                        ctypes.c_float(a["T"]), FAKE, a["acc"], FAKE, FAKE, FAKE, None, None,
+                        None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=3), INVALID),
+    (dict(B=0), INVALID),
+    (dict(N=9), UNSUPPORTED),
+    (dict(N=0), UNSUPPORTED),
+    (dict(V=1), UNSUPPORTED),
+    (dict(V=(1 << 20) + 1), UNSUPPORTED),
+    (dict(T=0.0), INVALID),
+    (dict(T=float("nan")), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(acc=None), INVALID),
+    (dict(wsb=16), WORKSPACE),
+])
+def test_verify_validation(L, kw, status):
+    assert ver(L, **kw) == status
+
+
+def test_verify_workspace_query(L):
+    assert L.isd_verify_workspace_bytes(64, 4, 151936) > 0
+    assert L.isd_verify_workspace_bytes(0, 4, 151936) == 0
+
+
+def proj(L, **kw):
+    a = dict(M=448, K=4096, Nout=4096, r=128, gate=FAKE, a=FAKE, b=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.isd_gated_lora_proj(FAKE, FAKE, a["a"], a["b"], a["gate"], FAKE, a["M"], a["K"],
+                                 a["Nout"], a["r"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), INVALID),
+    (dict(K=100), UNSUPPORTED),
+    (dict(Nout=200), UNSUPPORTED),
+    (dict(r=64), UNSUPPORTED),
+    (dict(a=None), INVALID),
+    (dict(wsb=1000), WORKSPACE),
+])
+def test_proj_validation(L, kw, status):
+    assert proj(L, **kw) == status
+
+
+def test_workspace_queries_grow_with_shape(L):
+    small = L.isd_attention_workspace_bytes(2, 4, 32, 8, 128, 512)
+    big = L.isd_attention_workspace_bytes(64, 4, 32, 8, 128, 4096)
+    assert 0 < small < big
+    assert L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 128) > \
+        L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 0) > 0

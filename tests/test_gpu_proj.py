@@ -1,0 +1,46 @@
+"""GPU parity of isd_gated_lora_proj: oracle tolerance, bit-identity of ungated rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from strided_verify_propose_amd import isd, synth
+from tests.helpers import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run(M, K, Nout, r, seed, pattern=(0, 0, 0, 1, 1, 1, 1)):
+    cfg = synth.ProjConfig("p", B=1, N=1, K=K, Nout=Nout, r=r, x_sd=1.0, w_sd=0.02, seed=seed,
+                           gate_pattern=pattern)
+    p = synth.proj_inputs(cfg, M=M)
+    print(f"projection case M={M} K={K} Nout={Nout} r={r}", flush=True)
+    x, w, a, b, gate = (to_dev(t) for t in (p.x, p.w, p.a, p.b, p.gate))
+    y = isd.gated_lora_proj(x, w, a, b, gate)
+    y2 = isd.gated_lora_proj(x, w, a, b, gate)
+    yb = isd.gated_lora_proj(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "not deterministic"
+    g = p.gate.astype(bool)
+    Y, Yb = to_np(y), to_np(yb)
+    assert np.array_equal(Y[~g], Yb[~g]), "ungated rows differ from the base-only call"
+    ref = oracle.gated_lora_proj(p.x, p.w, p.a, p.b, p.gate)
+    worst = assert_close(Y, ref, 2e-2, "gated projection")
+    assert_close(Yb, oracle.gated_lora_proj(p.x, p.w), 2e-2, "base projection")
+    print(f"  worst relative error {worst:.3e}", flush=True)
+
+
+def test_rlora_full_size():
+    """448 = 64 requests x 7 rows, K = Nout = 4096, rank 128, gate 0001111 per request."""
+    run(448, 4096, 4096, 128, 1004)
+
+
+@pytest.mark.parametrize("M,K,Nout,r", [(1, 64, 128, 128), (130, 512, 256, 128),
+                                        (7, 4096, 128, 256), (300, 1024, 640, 128)])
+def test_ragged_shapes(M, K, Nout, r):
+    run(M, K, Nout, r, 7 + M)
+
+
+def test_all_gated_and_none_gated():
+    run(64, 256, 128, 128, 3, pattern=(1,))
+    run(64, 256, 128, 128, 4, pattern=(0,))

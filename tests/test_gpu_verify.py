@@ -1,0 +1,114 @@
+"""GPU parity of isd_verify against the oracle, plus the exact laws through the kernel."""
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+from scipy.stats import chisquare
+
+import oracle
+from strided_verify_propose_amd import isd, synth
+from tests.helpers import RTOL, assert_close, to_dev, to_np, verify_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg(name, dtype, B, N, V, seed, anchor_sd=3.0, noise_sd=0.3, argmax=False):
+    return synth.StepConfig(name, dtype, B=B, N=N, Hq=1, Hkv=1, D=64, V=V, ctx=("fixed", 0),
+                            anchor_sd=anchor_sd, noise_sd=noise_sd, seed=seed, argmax_drafts=argmax)
+
+
+def run(c, temperature=1.0):
+    v = synth.verify_inputs(c)
+    print(f"verify case {c.name} dtype={c.dtype} B={c.B} N={c.N} V={c.V} argmax={c.argmax_drafts}", flush=True)
+    ref = oracle.verify_step(v.logits, v.draft_logits, v.draft_ids, v.uniforms, c.N, temperature)
+    out = isd.verify(to_dev(v.logits), None if v.draft_logits is None else to_dev(v.draft_logits),
+                     to_dev(v.draft_ids), to_dev(v.uniforms), temperature)
+    torch.cuda.synchronize()
+    compared, excluded = verify_parity(out, ref, c.N)
+    rt = RTOL[c.dtype]
+    assert_close(to_np(out["p_draft"]), ref["p_draft"], rt, "p_draft")
+    assert_close(to_np(out["q_draft"]), ref["q_draft"], rt, "q_draft")
+    R = c.R
+    nrows = R + (c.N - 1 if v.draft_logits is not None else 0)
+    assert_close(to_np(out["row_lse"])[:, :nrows], ref["row_lse"][:, :nrows], rt, "row_lse")
+    if v.draft_logits is None:
+        assert np.all(to_np(out["row_lse"])[:, R:] == 0)
+    print(f"  compared {compared} decisions/ids, excluded {excluded} near-threshold draws", flush=True)
+    return out, ref, compared, excluded
+
+
+CASES = [
+    cfg("tiny_fp32", "f32", 1, 2, 1024, 1000, anchor_sd=2.0, noise_sd=0.5),
+    cfg("tiny_fp32_argmax", "f32", 3, 2, 1024, 1010, anchor_sd=2.0, noise_sd=0.5, argmax=True),
+    cfg("bf16_v5000", "bf16", 16, 4, 5000, 11),
+    cfg("bf16_v300_unaligned", "bf16", 12, 3, 300, 12, anchor_sd=1.0, noise_sd=0.5),
+    cfg("f32_v301_unaligned", "f32", 12, 3, 301, 13, anchor_sd=1.0, noise_sd=0.5),
+    cfg("bf16_v8", "bf16", 64, 2, 8, 14, anchor_sd=1.0, noise_sd=1.0),
+    cfg("bf16_v40000_chunks", "bf16", 10, 4, 40000, 15),
+    cfg("bf16_n1", "bf16", 9, 1, 3000, 16),
+    cfg("bf16_n8", "bf16", 6, 8, 20000, 17, noise_sd=0.1),
+    cfg("bf16_argmax", "bf16", 16, 4, 33000, 18, argmax=True, noise_sd=0.05),
+    cfg("f32_big_noise", "f32", 16, 4, 17000, 19, noise_sd=2.0),
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c.name for c in CASES])
+def test_verify_parity(c):
+    run(c)
+
+
+def test_verify_temperature():
+    run(cfg("bf16_temp", "bf16", 8, 4, 9000, 21), temperature=0.7)
+
+
+def test_verify_qwen3_8b_full_size():
+    """B=64, N=4, vocab 151936, anchor N(0,3), proposal = anchor + N(0,0.3)."""
+    out, ref, compared, excluded = run(synth.QWEN3_8B)
+    assert compared > 64 * 4
+    acc = ref["n_accept"].mean()
+    print(f"  mean accepted drafts {acc:.2f} of 3", flush=True)
+
+
+def test_verify_q_equals_p_accepts_all():
+    c = cfg("qp", "bf16", 32, 4, 20000, 31)
+    v = synth.verify_inputs(c)
+    logits = v.logits.copy()
+    logits[:, :3] = v.draft_logits
+    out = isd.verify(to_dev(logits), to_dev(v.draft_logits), to_dev(v.draft_ids), to_dev(v.uniforms))
+    assert np.all(to_np(out["n_accept"]) == 3)
+    assert np.all(to_np(out["accept"]) == 1)
+
+
+def test_verify_deterministic():
+    c = cfg("det", "bf16", 16, 4, 151936, 41)
+    v = synth.verify_inputs(c)
+    args = (to_dev(v.logits), to_dev(v.draft_logits), to_dev(v.draft_ids), to_dev(v.uniforms))
+    a = isd.verify(*args)
+    b = isd.verify(*args)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("argmax", [False, True])
+def test_emitted_token_law_through_kernel(argmax):
+    """Chi-square on an 8-token vocab: the first emitted token follows p."""
+    rng = np.random.default_rng(7 + argmax)
+    V, n = 8, 60000
+    lp = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    lq = (lp + rng.standard_normal(V) * 0.9).astype(np.float32)
+    logits = np.tile(rng.standard_normal((1, 3, V)).astype(np.float32), (n, 1, 1))
+    logits[:, 0] = lp
+    if argmax:
+        d = np.full((n, 1), 5, np.int32)
+        dl = None
+    else:
+        d = rng.choice(V, size=(n, 1), p=softmax(lq.astype(np.float64))).astype(np.int32)
+        dl = to_dev(np.tile(lq, (n, 1, 1)))
+    u = (rng.integers(0, 1 << 24, size=(n, 3)) / float(1 << 24)).astype(np.float32)
+    out = isd.verify(to_dev(logits), dl, to_dev(d), to_dev(u))
+    acc = to_np(out["accept"])[:, 0]
+    first = np.where(acc == 1, d[:, 0], to_np(out["next_token"]))
+    p = softmax(lp.astype(np.float64))
+    stat = chisquare(np.bincount(first, minlength=V), p * n)
+    print(f"  chi-square {stat.statistic:.2f} (7 dof), p-value {stat.pvalue:.3g}", flush=True)
+    assert stat.statistic < 24.32       # 7 dof, alpha = 1e-3
