@@ -24,11 +24,9 @@
  *   - Results are bitwise reproducible for the same inputs and shapes (fixed reduction
  *     orders, no floating-point atomics).
  *   - Each entry point has its own workspace (device memory, caller-owned, at least the
- *     size its *_workspace_bytes query returns).  It must be ZERO-FILLED before its first
- *     use with a given set of shape arguments (where the completion counters sit depends
- *     on the shapes); every call that completes leaves its counters at zero again, so a
- *     workspace can be reused for the same shapes without clearing.  Calls that share a
- *     workspace must not run concurrently.
+ *     size its *_workspace_bytes query returns).  Its contents on entry do not matter
+ *     unless the entry point says otherwise.  Calls that share a workspace must not run
+ *     concurrently.
  *   - bf16 values are IEEE binary32 truncated to their upper 16 bits (uint16 storage).
  */
 #ifndef ISD_H

@@ -19,8 +19,9 @@
 //   * The split holding the block also writes the block's K/V rows into their page
 //     slots (after its own page loop) and attends to them from registers with the
 //     causal mask.  No other workgroup reads those slots.
-//   * Splits of one (request, head) write unnormalised partials; the last one to
-//     finish (a counter in the workspace) merges them in split order and writes out.
+//   * A request whose cached pages fit one split writes its output directly; otherwise
+//     each split writes an unnormalised partial (max, sum, O) and a small second kernel
+//     merges them in split order.  No workgroup waits on or signals another.
 #include "device.h"
 #include "launch.h"
 
@@ -46,7 +47,7 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kf)[D / 32], u32x2 (&v
                                             float (&l)[NQB], float scale_log2, int nvalid,
                                             int G, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
-  if (MODE == 1) {
+  if (MODE == 1 && nvalid < PAGE) {
     // invalid slots may hold anything: zero their V so P = 0 never meets a non-finite V
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
@@ -143,14 +144,20 @@ __device__ __forceinline__ void stash_state(const f32x4 (&o)[NQB][D / 16], const
   }
 }
 
+// Splits of the cached pages: nsplit = ceil(ceil(L/16) / pages_per_split), at least one.
+__device__ __forceinline__ int split_count(int L, int pps) {
+  const int ncp = (L + PAGE - 1) / PAGE;
+  return ncp == 0 ? 1 : (ncp + pps - 1) / pps;
+}
+
 template <int D, int NQB>
-__global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) {
+__global__ __launch_bounds__(THREADS, (NQB <= 2) ? 2 : 1) void attn_bf16_kernel(const AttnLaunch a) {
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   // device-side preconditions are clamped so a violation cannot address outside buffers
   const int L = min(max(a.ctx_lens[b], 0), a.max_ctx_len);
   const int ncp = (L + PAGE - 1) / PAGE;
   const int pps = a.pages_per_split;
-  const int nsplit = ncp == 0 ? 1 : (ncp + pps - 1) / pps;
+  const int nsplit = split_count(L, pps);
   if (s >= nsplit) return;
 
   const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
@@ -165,6 +172,11 @@ __global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) 
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
   const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
   const size_t tile = (size_t)PAGE * D;
+
+  // This wave's pages p0 + wave + 4i, i < npw: their physical ids, one per lane, read
+  // back as scalars so no page-table load sits between two page loads.
+  const int npw = (p1 - p0 - wave + 3) / 4;
+  const int my_id = (lane < npw) ? page_id(pt, p0 + wave + 4 * lane, a.num_pages) : 0;
 
   // Q^T fragments (B operand of S^T = K Q^T): query row 16 qb + l16, dims 32c + 8g ..
   u32x4 qf[NQB][D / 32];
@@ -192,32 +204,21 @@ __global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) 
     for (int n = 0; n < D / 16; ++n) o[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- cached pages: wave w takes pages p0 + w, p0 + w + 4, ...
-  int pg = p0 + wave;
-  u32x4 kf[D / 32];
-  u32x2 vf[D / 16];
-  if (pg < p1) {
-    const size_t base = ((size_t)page_id(pt, pg, a.num_pages) * Hkv + kvh) * tile;
-    load_kv_page<D>(kc + base, vc + base, lane, kf, vf);
-  }
-  for (; pg < p1; pg += 4) {
-    const int pn = pg + 4;
-    u32x4 kn[D / 32];
-    u32x2 vn[D / 16];
-    if (pn < p1) {
-      const size_t base = ((size_t)page_id(pt, pn, a.num_pages) * Hkv + kvh) * tile;
-      load_kv_page<D>(kc + base, vc + base, lane, kn, vn);
-    }
-    const int nvalid = L - pg * PAGE;
-    if (nvalid >= PAGE)
-      attend_tile<D, NQB, 0>(kf, vf, qf, o, m, l, scale_log2, PAGE, G, lane);
-    else
-      attend_tile<D, NQB, 1>(kf, vf, qf, o, m, l, scale_log2, nvalid, G, lane);
-    if (pn < p1) {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) kf[c] = kn[c];
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n) vf[n] = vn[n];
+  // ---- cached pages, two in flight: buffers A (even i) and B (odd i)
+  auto tile_base = [&](int i) -> size_t {
+    const int pid = __builtin_amdgcn_readlane(my_id, i);
+    return ((size_t)pid * Hkv + kvh) * tile;
+  };
+  u32x4 kA[D / 32], kB[D / 32];
+  u32x2 vA[D / 16], vB[D / 16];
+  if (npw > 0) { const size_t t0 = tile_base(0); load_kv_page<D>(kc + t0, vc + t0, lane, kA, vA); }
+  if (npw > 1) { const size_t t1 = tile_base(1); load_kv_page<D>(kc + t1, vc + t1, lane, kB, vB); }
+  for (int i = 0; i < npw; i += 2) {
+    attend_tile<D, NQB, 1>(kA, vA, qf, o, m, l, scale_log2, L - (p0 + wave + 4 * i) * PAGE, G, lane);
+    if (i + 2 < npw) { const size_t t = tile_base(i + 2); load_kv_page<D>(kc + t, vc + t, lane, kA, vA); }
+    if (i + 1 < npw) {
+      attend_tile<D, NQB, 1>(kB, vB, qf, o, m, l, scale_log2, L - (p0 + wave + 4 * (i + 1)) * PAGE, G, lane);
+      if (i + 3 < npw) { const size_t t = tile_base(i + 3); load_kv_page<D>(kc + t, vc + t, lane, kB, vB); }
     }
   }
 
@@ -227,11 +228,9 @@ __global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) 
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
   const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
   if (last && wave == ((p1 - p0) & 3)) {
-    u32x4 kb[D / 32];
-    u32x2 vb[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      kb[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
+      kA[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
                         : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
@@ -241,10 +240,10 @@ __global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) 
         const int t = 4 * g + i;
         h[i] = (t < R) ? vn_[blk + t * rstride + 16 * n + l16] : 0u;
       }
-      vb[n][0] = h[0] | (h[1] << 16);
-      vb[n][1] = h[2] | (h[3] << 16);
+      vA[n][0] = h[0] | (h[1] << 16);
+      vA[n][1] = h[2] | (h[3] << 16);
     }
-    attend_tile<D, NQB, 2>(kb, vb, qf, o, m, l, scale_log2, 0, G, lane);
+    attend_tile<D, NQB, 2>(kA, vA, qf, o, m, l, scale_log2, 0, G, lane);
   }
 
   // ---- merge the four waves in LDS: (w0 + w2) + (w1 + w3)
@@ -263,95 +262,119 @@ __global__ __launch_bounds__(THREADS) void attn_bf16_kernel(const AttnLaunch a) 
   __syncthreads();
 
   // ---- append the block rows to their page slots (after every read of this split's pages)
-  {
+  if (last) {
     uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
     uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    if (last) {
-      // K: 16-byte units of 8 dims; V: single elements
-      for (int e = threadIdx.x; e < R * (D / 8); e += THREADS) {
-        const int t = e / (D / 8), d8 = e - t * (D / 8);
-        const int j = L + t;
-        const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-        *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) =
-            *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
-      }
-      for (int e = threadIdx.x; e < R * D; e += THREADS) {
-        const int t = e / D, d = e - t * D;
-        const int j = L + t, slot = j % PAGE;
-        const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-        vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] =
-            vn_[blk + t * rstride + d];
-      }
+    // K: 16-byte units of 8 dims; V: single elements
+    for (int e = threadIdx.x; e < R * (D / 8); e += THREADS) {
+      const int t = e / (D / 8), d8 = e - t * (D / 8);
+      const int j = L + t;
+      const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
+      *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) =
+          *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
+    }
+    for (int e = threadIdx.x; e < R * D; e += THREADS) {
+      const int t = e / D, d = e - t * D;
+      const int j = L + t, slot = j % PAGE;
+      const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
+      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] =
+          vn_[blk + t * rstride + d];
     }
   }
 
-  if (wave == 0) {
-    merge_state<D, NQB>(o, m, l, sm[0], sl[0], so[0], lane);
-    if (nsplit == 1) {
-      uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (wave != 0) return;
+  merge_state<D, NQB>(o, m, l, sm[0], sl[0], so[0], lane);
+  if (nsplit == 1) {
+    uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qr = qb * 16 + l16;
-        if (qr >= RG) continue;
-        const int r = qr / G, hg = qr - r * G;
-        const float inv = 1.f / l[qb];
-        uint16_t* op = out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * g;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qr = qb * 16 + l16;
+      if (qr >= RG) continue;
+      const int r = qr / G, hg = qr - r * G;
+      const float inv = 1.f / l[qb];
+      uint16_t* op = out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * g;
 #pragma unroll
-        for (int n = 0; n < D / 16; ++n) {
-          u32x2 w;
-          w[0] = pack_bf16x2(o[qb][n][0] * inv, o[qb][n][1] * inv);
-          w[1] = pack_bf16x2(o[qb][n][2] * inv, o[qb][n][3] * inv);
-          *reinterpret_cast<u32x2*>(op + 16 * n) = w;
-        }
+      for (int n = 0; n < D / 16; ++n) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[qb][n][0] * inv, o[qb][n][1] * inv);
+        w[1] = pack_bf16x2(o[qb][n][2] * inv, o[qb][n][3] * inv);
+        *reinterpret_cast<u32x2*>(op + 16 * n) = w;
       }
-    } else {
-      const size_t slot = ((size_t)b * Hkv + kvh) * a.splits_max + s;
-      float* po = a.part_o + slot * RG * D;
-      float* pml = a.part_ml + slot * RG * 2;
+    }
+  } else {
+    // unnormalised partial state of this split; the combine kernel merges them
+    const size_t slot = ((size_t)b * Hkv + kvh) * a.splits_max + s;
+    float* po = a.part_o + slot * RG * D;
+    float* pml = a.part_ml + slot * RG * 2;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qr = qb * 16 + l16;
-        if (qr >= RG) continue;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qr = qb * 16 + l16;
+      if (qr >= RG) continue;
 #pragma unroll
-        for (int n = 0; n < D / 16; ++n)
-          *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = o[qb][n];
-        if (g == 0) {
-          pml[qr * 2] = m[qb];
-          pml[qr * 2 + 1] = l[qb];
-        }
+      for (int n = 0; n < D / 16; ++n)
+        *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = o[qb][n];
+      if (g == 0) {
+        pml[qr * 2] = m[qb];
+        pml[qr * 2 + 1] = l[qb];
       }
-      __threadfence();
     }
   }
-  if (nsplit == 1) return;
+}
 
-  // ---- the last split of this (request, head) to finish merges all partials in order
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[b * Hkv + kvh], 1u);
-    s_last = (prev == (uint32_t)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t slot0 = ((size_t)b * Hkv + kvh) * a.splits_max;
+// Merge the split partials of one (request, KV head) in split order.  Only requests whose
+// cached pages span more than one split have work here.
+constexpr int COMBINE_BATCH = 8;
+
+template <int D>
+__global__ __launch_bounds__(THREADS) void attn_combine_kernel(const AttnLaunch a) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int L = min(max(a.ctx_lens[b], 0), a.max_ctx_len);
+  const int nsplit = split_count(L, a.pages_per_split);
+  if (nsplit <= 1) return;
+  const int R = a.R, G = a.G, Hq = a.Hq, RG = R * G;
+  const size_t slot0 = ((size_t)b * a.Hkv + kvh) * a.splits_max;
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int e = threadIdx.x; e < RG * D; e += THREADS) {
-    const int qr = e / D, d = e - qr * D;
+  for (int it = threadIdx.x; it < RG * (D / 4); it += THREADS) {
+    const int qr = it / (D / 4), d4 = it - qr * (D / 4);
     float M = neg_inf();
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, a.part_ml[((slot0 + sp) * RG + qr) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* ml = a.part_ml + ((slot0 + sp) * RG + qr) * 2;
-      const float f = exp2_hw(ml[0] - M);
-      den += f * ml[1];
-      num += f * a.part_o[((slot0 + sp) * RG + qr) * D + d];
+    for (int s0 = 0; s0 < nsplit; s0 += COMBINE_BATCH) {
+      float mv[COMBINE_BATCH];
+#pragma unroll
+      for (int k = 0; k < COMBINE_BATCH; ++k)
+        mv[k] = (s0 + k < nsplit) ? a.part_ml[((slot0 + s0 + k) * RG + qr) * 2] : neg_inf();
+#pragma unroll
+      for (int k = 0; k < COMBINE_BATCH; ++k) M = fmaxf(M, mv[k]);
     }
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += COMBINE_BATCH) {
+      f32x4 ov[COMBINE_BATCH];
+      float mv[COMBINE_BATCH], lv[COMBINE_BATCH];
+#pragma unroll
+      for (int k = 0; k < COMBINE_BATCH; ++k) {
+        if (s0 + k < nsplit) {
+          const size_t sl = slot0 + s0 + k;
+          ov[k] = *reinterpret_cast<const f32x4*>(a.part_o + (sl * RG + qr) * D + 4 * d4);
+          mv[k] = a.part_ml[(sl * RG + qr) * 2];
+          lv[k] = a.part_ml[(sl * RG + qr) * 2 + 1];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < COMBINE_BATCH; ++k) {
+        if (s0 + k < nsplit) {
+          const float f = exp2_hw(mv[k] - M);
+          den += f * lv[k];
+          num += f * ov[k];
+        }
+      }
+    }
+    const float inv = 1.f / den;
     const int r = qr / G, hg = qr - r * G;
-    out[(((size_t)b * R + r) * Hq + kvh * G + hg) * D + d] = (uint16_t)f32_to_bf16_bits(num / den);
+    u32x2 w;
+    w[0] = pack_bf16x2(num[0] * inv, num[1] * inv);
+    w[1] = pack_bf16x2(num[2] * inv, num[3] * inv);
+    *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = w;
   }
-  if (threadIdx.x == 0) a.counters[b * Hkv + kvh] = 0u;
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -454,6 +477,7 @@ hipError_t launch_bf16(const AttnLaunch& a, hipStream_t s) {
     case 4: attn_bf16_kernel<D, 4><<<grid, THREADS, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  if (a.splits_max > 1) attn_combine_kernel<D><<<dim3(a.Hkv, a.B), THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---------------------------------------------------------------- attention workspace
 struct AttnWs {
   int pps, splits_max;
-  size_t counters, part_o, part_ml, total;
+  size_t part_o, part_ml, total;
 };
 
 AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
@@ -51,8 +51,7 @@ AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
   w.pps = isd::attention_pages_per_split(B, Hkv, max_ctx_len, R);
   w.splits_max = ncp == 0 ? 1 : (ncp + w.pps - 1) / w.pps;
   const size_t slots = (size_t)B * Hkv * w.splits_max;
-  w.counters = 0;
-  w.part_o = align256((size_t)B * Hkv * sizeof(uint32_t));
+  w.part_o = 0;
   w.part_ml = w.part_o + align256(slots * RG * D * sizeof(float));
   w.total = w.part_ml + align256(slots * RG * 2 * sizeof(float));
   return w;
@@ -80,35 +79,17 @@ VerWs ver_ws(int B, int N, int V) {
 }
 
 // ---------------------------------------------------------------- projection workspace
-int gemm_splits(int M, int N, int K) {
-  const int kb = K / isd::GEMM_BK;
-  if (const char* e = getenv("ISD_GEMM_SPLITS")) {
-    const int s = atoi(e);
-    if (s >= 1 && kb % s == 0) return s;
-  }
-  const long tiles = (long)((M + isd::GEMM_BM - 1) / isd::GEMM_BM) * (N / isd::GEMM_BN);
-  int s = 1;
-  while (tiles * s < 256 && s < 16 && kb % (2 * s) == 0 && kb / (2 * s) >= 4) s *= 2;
-  return s;
-}
-
 struct ProjWs {
-  int s_main, s_down;
-  size_t T, part, cnt_main, cnt_down, total;
+  size_t ybase, T, total;
 };
 
 ProjWs proj_ws(int M, int K, int Nout, int r) {
+  (void)K;
   ProjWs w{};
-  w.s_main = gemm_splits(M, Nout, K);
-  w.s_down = r > 0 ? gemm_splits(M, r, K) : 1;
-  const size_t tm = (M + isd::GEMM_BM - 1) / isd::GEMM_BM;
-  const size_t part_main = w.s_main > 1 ? (size_t)w.s_main * M * Nout : 0;
-  const size_t part_down = (r > 0 && w.s_down > 1) ? (size_t)w.s_down * M * r : 0;
-  w.cnt_main = 0;
-  w.cnt_down = align256(tm * (Nout / isd::GEMM_BN) * sizeof(uint32_t));
-  w.T = w.cnt_down + align256(tm * (r > 0 ? (size_t)(r / isd::GEMM_BN) : 1) * sizeof(uint32_t));
-  w.part = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
-  w.total = w.part + align256((part_main > part_down ? part_main : part_down) * sizeof(float));
+  w.ybase = 0;
+  w.T = align256(r > 0 ? (size_t)M * Nout * sizeof(float) : 0);
+  w.total = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
+  if (w.total == 0) w.total = 256;
   return w;
 }
 
@@ -164,7 +145,7 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   if (dt == ISD_F32 && max_ctx_len + R > 16384)
     return fail(ISD_ERR_UNSUPPORTED, "attention: f32 path holds at most 16384 tokens");
   const AttnWs w = attn_ws(B, N, Hq, Hkv, D, max_ctx_len);
-  if (dt == ISD_BF16 && (!workspace || workspace_bytes < w.total))
+  if (dt == ISD_BF16 && w.splits_max > 1 && (!workspace || workspace_bytes < w.total))
     return fail(ISD_ERR_WORKSPACE, "attention: workspace %zu bytes, need %zu", workspace_bytes, w.total);
 
   isd::AttnLaunch a{};
@@ -175,7 +156,6 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages; a.max_ctx_len = max_ctx_len; a.scale = scale;
   a.pages_per_split = w.pps; a.splits_max = w.splits_max;
   char* ws = static_cast<char*>(workspace);
-  a.counters = ws ? reinterpret_cast<uint32_t*>(ws + w.counters) : nullptr;
   a.part_o = ws ? reinterpret_cast<float*>(ws + w.part_o) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(ws + w.part_ml) : nullptr;
   return hip_status(isd::launch_attention(a, static_cast<hipStream_t>(stream)), "attention launch");
@@ -250,37 +230,23 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
       return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj: r=%d (supported: 128, 256)", r);
   }
   const ProjWs ws_ = proj_ws(M, K, Nout, lora ? r : 0);
-  if (!workspace || workspace_bytes < ws_.total)
+  if (lora && (!workspace || workspace_bytes < ws_.total))
     return fail(ISD_ERR_WORKSPACE, "gated_lora_proj: workspace %zu bytes, need %zu", workspace_bytes, ws_.total);
   char* ws = static_cast<char*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* T = reinterpret_cast<uint16_t*>(ws + ws_.T);
-  float* part = reinterpret_cast<float*>(ws + ws_.part);
+  isd::ProjLaunch p{};
+  p.X = static_cast<const uint16_t*>(x);
+  p.W = static_cast<const uint16_t*>(w);
+  p.Y = static_cast<uint16_t*>(y);
+  p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
   if (lora) {
-    isd::GemmLaunch d{};
-    d.A = static_cast<const uint16_t*>(x);
-    d.B = static_cast<const uint16_t*>(a);
-    d.M = M; d.N = r; d.K = K; d.splits = ws_.s_down;
-    d.part = part;
-    d.counters = reinterpret_cast<uint32_t*>(ws + ws_.cnt_down);
-    d.C = T;
-    hipError_t e = isd::launch_gemm(d, s);
-    if (e != hipSuccess) return hip_status(e, "gated_lora_proj down-projection launch");
+    p.A = static_cast<const uint16_t*>(a);
+    p.Bl = static_cast<const uint16_t*>(b);
+    p.gate = gate;
+    p.r = r;
+    p.Ybase = reinterpret_cast<float*>(ws + ws_.ybase);
+    p.T = reinterpret_cast<uint16_t*>(ws + ws_.T);
   }
-  isd::GemmLaunch g{};
-  g.A = static_cast<const uint16_t*>(x);
-  g.B = static_cast<const uint16_t*>(w);
-  g.M = M; g.N = Nout; g.K = K; g.splits = ws_.s_main;
-  g.part = part;
-  g.counters = reinterpret_cast<uint32_t*>(ws + ws_.cnt_main);
-  g.C = static_cast<uint16_t*>(y);
-  if (lora) {
-    g.T = T;
-    g.Bl = static_cast<const uint16_t*>(b);
-    g.gate = gate;
-    g.r = r;
-  }
-  return hip_status(isd::launch_gemm(g, s), "gated_lora_proj launch");
+  return hip_status(isd::launch_proj(p, static_cast<hipStream_t>(stream)), "gated_lora_proj launch");
 }
 
 }  // extern "C"

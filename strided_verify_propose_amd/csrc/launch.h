@@ -26,7 +26,6 @@ struct AttnLaunch {
   int pages_per_split;   // cached pages handled by one workgroup (multiple of 4)
   int splits_max;        // grid extent over splits
   // workspace carve-up
-  uint32_t* counters;    // [B*Hkv], zero between calls
   float* part_o;         // [B*Hkv*splits_max][R*G][D]
   float* part_ml;        // [B*Hkv*splits_max][R*G][2]
 };
@@ -73,21 +72,17 @@ struct VerifyLaunch {
 hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);
 
 // ---------------------------------------------------------------- gated projection
-struct GemmLaunch {
-  const uint16_t* A;            // [M, K]
-  const uint16_t* B;            // [N, K]
-  int M, N, K;
-  int splits;                   // split-K factor (K/splits multiple of 64)
-  float* part;                  // [splits][M][N] fp32 (splits > 1)
-  uint32_t* counters;           // [tiles_m * tiles_n] (splits > 1)
-  uint16_t* C;                  // [M, N] bf16 output
-  // optional LoRA epilogue: C += gate ? T * Bl^T : 0
-  const uint16_t* T;            // [M, r] bf16
-  const uint16_t* Bl;           // [N, r]
-  const uint8_t* gate;          // [M]
-  int r;
+struct ProjLaunch {
+  const uint16_t* X;            // [M, K]
+  const uint16_t* W;            // [Nout, K]  (W^T)
+  const uint16_t* A;            // [r, K]     (A^T), null when ungated
+  const uint16_t* Bl;           // [Nout, r]  (B^T), null when ungated
+  const uint8_t* gate;          // [M] or null (base only)
+  uint16_t* Y;                  // [M, Nout] bf16
+  int M, K, Nout, r;            // r = 0 when ungated
+  float* Ybase;                 // workspace [M, Nout] fp32 (rows with gate 1)
+  uint16_t* T;                  // workspace [M, r] bf16
 };
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
-constexpr int GEMM_BM = 128, GEMM_BN = 128, GEMM_BK = 64;
+hipError_t launch_proj(const ProjLaunch& p, hipStream_t s);
 
 }  // namespace isd

@@ -63,8 +63,8 @@ def att(L, **kw):
     (dict(maxctx=-1), INVALID),
     (dict(N=10, Hq=32, Hkv=4, maxp=100), UNSUPPORTED),   # 19 rows * 8 heads > 64
     (dict(scale=float("inf")), INVALID),
-    (dict(wsb=100), WORKSPACE),
-    (dict(ws=None), WORKSPACE),
+    (dict(wsb=100, maxctx=3000, maxp=200), WORKSPACE),   # long enough to need splits
+    (dict(ws=None, maxctx=3000, maxp=200), WORKSPACE),
     (dict(dt=0, maxctx=20000, maxp=2000), UNSUPPORTED),  # f32 path token limit
 ])
 def test_attention_validation(L, kw, status):
