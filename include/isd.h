@@ -81,11 +81,12 @@ const char* isd_last_error(void);
  *   KV head h / G.  The block's own keys are used as written, so the result equals attention
  *   read entirely through the pages after the append.  Rejected tokens are rolled back by the
  *   caller simply not advancing ctx_lens; their slots are overwritten by the next step.
- * Requires: page_size == 16, D in {64, 128}, Hq % Hkv == 0, R*G <= 64 (bf16) / any (f32),
+ * Requires: page_size == 16, D in {64, 128}, Hq % Hkv == 0,
  *   every page the request touches (ctx_lens[b]+R tokens) present in its page table,
  *   0 <= ctx_lens[b] <= max_ctx_len, max_ctx_len + R <= 16*max_pages_per_seq;
- *   for ISD_F32 also max_ctx_len + R <= 16384.
- * scale: usually 1/sqrt(D). */
+ *   for ISD_BF16 also R*G <= 64, N <= 8 and B <= 2048; for ISD_F32 max_ctx_len + R <= 16384.
+ * scale: usually 1/sqrt(D).  Workspace: isd_attention_workspace_bytes (bf16 only; the
+ *   f32 path needs none). */
 size_t isd_attention_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_ctx_len);
 isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, const void* v_new,
                               void* k_cache, void* v_cache, const int32_t* page_table,

@@ -19,9 +19,15 @@
 //   * The split holding the block also writes the block's K/V rows into their page
 //     slots (after its own page loop) and attends to them from registers with the
 //     causal mask.  No other workgroup reads those slots.
-//   * A request whose cached pages fit one split writes its output directly; otherwise
-//     each split writes an unnormalised partial (max, sum, O) and a small second kernel
-//     merges them in split order.  No workgroup waits on or signals another.
+//   * Work is balanced tile by tile: the (request, KV head, page) units are laid out in
+//     one list and every workgroup of a grid sized to the resident capacity takes an
+//     equal contiguous slice.  A workgroup writes the output of every item it holds whole,
+//     and an unnormalised partial (max, sum, O) for the at most two items cut by its slice
+//     edges; a second kernel merges those in workgroup order and appends the block's K/V
+//     to the cache after all reads.  No workgroup waits on or signals another.
+#include <algorithm>
+#include <cstdlib>
+
 #include "device.h"
 #include "launch.h"
 
@@ -37,68 +43,85 @@ __device__ __forceinline__ int page_id(const int32_t* pt, int j, int num_pages) 
   return min(max(pt[j], 0), num_pages - 1);
 }
 
-// One 16-token tile (a cached page or the block) against every query block.
+// Query rows handled per wave and wave groups per workgroup.  Each wave keeps up to two
+// 16-row query blocks in registers; with more blocks (many query heads per KV head) a
+// second group of four waves takes the rest and reads the same pages, the repeats
+// hitting cache.
+template <int NQB>
+struct AttnShape {
+  static constexpr int QB = NQB < 2 ? NQB : 2;
+  static constexpr int GROUPS = (NQB + QB - 1) / QB;
+  static constexpr int THREADS = 256 * GROUPS;
+};
+
+// One 16-token tile (a cached page or the block) against this wave's query blocks.
 // MODE 0: all tokens valid.  MODE 1: tokens t < nvalid valid.  MODE 2: block tile,
 // token t valid for query row q iff t <= q / G (causal, diagonal included).
-template <int D, int NQB, int MODE>
+// Q^T fragments come from LDS: qs[qb][c][lane].
+template <int D, int QB, int MODE>
 __device__ __forceinline__ void attend_tile(const u32x4 (&kf)[D / 32], u32x2 (&vf)[D / 16],
-                                            const u32x4 (&qf)[NQB][D / 32],
-                                            f32x4 (&o)[NQB][D / 16], float (&m)[NQB],
-                                            float (&l)[NQB], float scale_log2, int nvalid,
+                                            const u32x4* __restrict__ qs, int qb0, int nqb,
+                                            f32x4 (&o)[QB][D / 16], float (&m)[QB],
+                                            float (&l)[QB], float scale_log2, int nvalid,
                                             int G, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
-  if (MODE == 1 && nvalid < PAGE) {
+  if (MODE == 1) {
     // invalid slots may hold anything: zero their V so P = 0 never meets a non-finite V
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (4 * g + i >= nvalid) {
-          uint32_t w = vf[n][i >> 1];
+          const uint32_t w = vf[n][i >> 1];
           vf[n][i >> 1] = (i & 1) ? (w & 0x0000ffffu) : (w & 0xffff0000u);
         }
       }
     }
   }
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
+  for (int j = 0; j < QB; ++j) {
+    const int qb = qb0 + j;
+    if (qb >= nqb) break;
+    // keep each block's Q fragment reads next to their use (register pressure)
+    if (j > 0) __builtin_amdgcn_sched_barrier(0);
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) st = mfma16x16x32(kf[c], qf[qb][c], st);
-    // st[i] = S^T[token 4g+i][query row 16 qb + l16]
-    float s[4];
+    for (int c = 0; c < D / 32; ++c)
+      st = mfma16x16x32(kf[c], qs[(qb * (D / 32) + c) * 64 + lane], st);
+    // st[i] = S^T[token 4g+i][query row 16 qb + l16] (unscaled)
+    if (MODE != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      bool ok = true;
-      if (MODE == 1) ok = t < nvalid;
-      if (MODE == 2) ok = t <= (qb * 16 + l16) / G;
-      s[i] = ok ? st[i] * scale_log2 : neg_inf();
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        const bool ok = (MODE == 1) ? (t < nvalid) : (t <= (qb * 16 + l16) / G);
+        st[i] = ok ? st[i] : neg_inf();
+      }
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m[qb], mx);
-    const float alpha = (m[qb] == neg_inf()) ? 0.f : exp2_hw(m[qb] - mnew);
+    const float mx = row4_max(fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3])));
+    const float mold = m[j];
+    const float mnew = fmaxf(mold, mx * scale_log2);  // running max in log2 units
+    // rescale O only when some query row's maximum moved (rare after the first pages)
+    if (__builtin_amdgcn_ballot_w64(mnew > mold)) {
+      const float alpha = (mold == neg_inf()) ? 0.f : exp2_hw(mold - mnew);
+      l[j] *= alpha;
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) o[j][n] *= alpha;
+    }
+    m[j] = mnew;
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2_hw(s[i] - mnew);
-    l[qb] = l[qb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m[qb] = mnew;
+    for (int i = 0; i < 4; ++i) p[i] = exp2_hw(fmaf(st[i], scale_log2, -mnew));
+    l[j] += (p[0] + p[1]) + (p[2] + p[3]);
     u32x2 pb;
-    pb[0] = pack_bf16x2(p[0], p[1]);
-    pb[1] = pack_bf16x2(p[2], p[3]);
+    pb[0] = cvt_pk_bf16(p[0], p[1]);
+    pb[1] = cvt_pk_bf16(p[2], p[3]);
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      o[qb][n] *= alpha;
-      o[qb][n] = mfma16x16x16(vf[n], pb, o[qb][n]);
-    }
+    for (int n = 0; n < D / 16; ++n) o[j][n] = mfma16x16x16(vf[n], pb, o[j][n]);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_kv_page(const uint16_t* __restrict__ kt,
-                                             const uint16_t* __restrict__ vt, int lane,
+__device__ __forceinline__ void load_kv_page(const uint16_t* kt, const uint16_t* vt, int lane,
                                              u32x4 (&kf)[D / 32], u32x2 (&vf)[D / 16]) {
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
@@ -108,272 +131,355 @@ __device__ __forceinline__ void load_kv_page(const uint16_t* __restrict__ kt,
     vf[n] = *reinterpret_cast<const u32x2*>(vt + n * 256 + lane * 4);
 }
 
-template <int D, int NQB>
-__device__ __forceinline__ void merge_state(f32x4 (&o)[NQB][D / 16], float (&m)[NQB],
-                                            float (&l)[NQB], const float* om, const float* ol,
-                                            const float* oo, int lane) {
+// Wave state <-> LDS (one wave's worth), lane-contiguous so every access is conflict-free.
+template <int D, int QB>
+__device__ __forceinline__ void stash_state(const f32x4 (&o)[QB][D / 16], const float (&m)[QB],
+                                            const float (&l)[QB], float* buf, int lane) {
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float mb = om[qb * 64 + lane];
+  for (int j = 0; j < QB; ++j) {
+    buf[(j * 2) * 64 + lane] = m[j];
+    buf[(j * 2 + 1) * 64 + lane] = l[j];
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) buf[(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane] = o[j][n][i];
+  }
+}
+template <int D, int QB>
+__device__ __forceinline__ void merge_state(f32x4 (&o)[QB][D / 16], float (&m)[QB], float (&l)[QB],
+                                            const float* buf, int lane) {
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const float mb = buf[(j * 2) * 64 + lane];
     if (mb == neg_inf()) continue;
-    const float M = fmaxf(m[qb], mb);
-    const float fa = (m[qb] == neg_inf()) ? 0.f : exp2_hw(m[qb] - M);
+    const float M = fmaxf(m[j], mb);
+    const float fa = (m[j] == neg_inf()) ? 0.f : exp2_hw(m[j] - M);
     const float fb = exp2_hw(mb - M);
-    l[qb] = fa * l[qb] + fb * ol[qb * 64 + lane];
-    m[qb] = M;
+    l[j] = fa * l[j] + fb * buf[(j * 2 + 1) * 64 + lane];
+    m[j] = M;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[qb][n][i] = fa * o[qb][n][i] + fb * oo[((qb * (D / 16) + n) * 4 + i) * 64 + lane];
+        o[j][n][i] = fa * o[j][n][i] + fb * buf[(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane];
   }
 }
 
-template <int D, int NQB>
-__device__ __forceinline__ void stash_state(const f32x4 (&o)[NQB][D / 16], const float (&m)[NQB],
-                                            const float (&l)[NQB], float* om, float* ol,
-                                            float* oo, int lane) {
+// ---------------------------------------------------------------- balanced work list
+// The flattened work list holds, for request b and KV head h, u_b = ceil(L_b/16) + 1
+// units: the cached pages in order, then the block's own rows.  Item (b, h) occupies
+// units [pre[b] + h u_b, pre[b] + (h+1) u_b) where pre is the exclusive prefix of Hkv u_b.
+// Workgroup w of a grid of W takes units [w T / W, (w+1) T / W): every workgroup gets the
+// same number of 16-token tiles, whatever the spread of context lengths.
+constexpr int MAX_B = 2048;  // requests per call on the bf16 path (prefix kept in LDS)
+
+__device__ __forceinline__ int units_of(int L) { return (L + PAGE - 1) / PAGE + 1; }
+
+__device__ __forceinline__ int clamp_len(const AttnLaunch& a, int b) {
+  return min(max(a.ctx_lens[b], 0), a.max_ctx_len);
+}
+
+// pre[0..B] in LDS (exclusive prefix of Hkv * u_b); wave 0 builds it.  Ends with a barrier.
+__device__ void build_prefix(const AttnLaunch& a, int* pre) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (a.B + 63) / 64;
+    const int b0 = min(a.B, lane * per), b1 = min(a.B, b0 + per);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += a.Hkv * units_of(clamp_len(a, b));
+    int incl = sum;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    om[qb * 64 + lane] = m[qb];
-    ol[qb * 64 + lane] = l[qb];
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oo[((qb * (D / 16) + n) * 4 + i) * 64 + lane] = o[qb][n][i];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int run = incl - sum;
+    for (int b = b0; b < b1; ++b) {
+      pre[b] = run;
+      run += a.Hkv * units_of(clamp_len(a, b));
+    }
+    if (lane == 63) pre[a.B] = incl;
   }
+  __syncthreads();
 }
 
-// Splits of the cached pages: nsplit = ceil(ceil(L/16) / pages_per_split), at least one.
-__device__ __forceinline__ int split_count(int L, int pps) {
-  const int ncp = (L + PAGE - 1) / PAGE;
-  return ncp == 0 ? 1 : (ncp + pps - 1) / pps;
+// largest b in [0, B) with pre[b] <= x
+__device__ __forceinline__ int find_request(const int* pre, int B, int x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int range_lo(int w, int T, int W) {
+  return (int)(((long long)w * T) / W);
 }
 
 template <int D, int NQB>
-__global__ __launch_bounds__(THREADS, (NQB <= 2) ? 2 : 1) void attn_bf16_kernel(const AttnLaunch a) {
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  // device-side preconditions are clamped so a violation cannot address outside buffers
-  const int L = min(max(a.ctx_lens[b], 0), a.max_ctx_len);
-  const int ncp = (L + PAGE - 1) / PAGE;
-  const int pps = a.pages_per_split;
-  const int nsplit = split_count(L, pps);
-  if (s >= nsplit) return;
+__global__ __launch_bounds__(AttnShape<NQB>::THREADS, (AttnShape<NQB>::QB == 1) ? 4 : 3)
+void attn_bf16_kernel(const AttnLaunch a) {
+  constexpr int QB = AttnShape<NQB>::QB;
+  constexpr int GROUPS = AttnShape<NQB>::GROUPS;
+  constexpr int NT = AttnShape<NQB>::THREADS;
+  constexpr int STATE = (2 * QB + QB * (D / 16) * 4) * 64;  // floats per stashed wave state
+  __shared__ int pre[MAX_B + 1];
+  __shared__ u32x4 qs[NQB * (D / 32) * 64];
+  __shared__ float st_buf[GROUPS][STATE];
+
+  build_prefix(a, pre);
+  const int T = pre[a.B];
+  const int W = gridDim.x, w = blockIdx.x;
+  const int lo = range_lo(w, T, W), hi = range_lo(w + 1, T, W);
 
   const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave >> 2, wg = wave & 3;  // wave group, wave within the group
+  const int qb0 = grp * QB;                  // this group's first query block
   const int l16 = lane & 15, g = lane >> 4;
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  const bool last = (s == nsplit - 1);
-  const int p0 = s * pps, p1 = min(ncp, p0 + pps);
-
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-  const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
-  const size_t tile = (size_t)PAGE * D;
-
-  // This wave's pages p0 + wave + 4i, i < npw: their physical ids, one per lane, read
-  // back as scalars so no page-table load sits between two page loads.
-  const int npw = (p1 - p0 - wave + 3) / 4;
-  const int my_id = (lane < npw) ? page_id(pt, p0 + wave + 4 * lane, a.num_pages) : 0;
-
-  // Q^T fragments (B operand of S^T = K Q^T): query row 16 qb + l16, dims 32c + 8g ..
-  u32x4 qf[NQB][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qr = qb * 16 + l16;
-    if (qr < RG) {
-      const int r = qr / G, hg = qr - r * G;
-      const uint16_t* qp = q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 8 * g;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[qb][c] = *reinterpret_cast<const u32x4*>(qp + 32 * c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[qb][c] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  f32x4 o[NQB][D / 16];
-  float m[NQB], l[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = neg_inf();
-    l[qb] = 0.f;
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n) o[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // ---- cached pages, two in flight: buffers A (even i) and B (odd i)
-  auto tile_base = [&](int i) -> size_t {
-    const int pid = __builtin_amdgcn_readlane(my_id, i);
-    return ((size_t)pid * Hkv + kvh) * tile;
-  };
-  u32x4 kA[D / 32], kB[D / 32];
-  u32x2 vA[D / 16], vB[D / 16];
-  if (npw > 0) { const size_t t0 = tile_base(0); load_kv_page<D>(kc + t0, vc + t0, lane, kA, vA); }
-  if (npw > 1) { const size_t t1 = tile_base(1); load_kv_page<D>(kc + t1, vc + t1, lane, kB, vB); }
-  for (int i = 0; i < npw; i += 2) {
-    attend_tile<D, NQB, 1>(kA, vA, qf, o, m, l, scale_log2, L - (p0 + wave + 4 * i) * PAGE, G, lane);
-    if (i + 2 < npw) { const size_t t = tile_base(i + 2); load_kv_page<D>(kc + t, vc + t, lane, kA, vA); }
-    if (i + 1 < npw) {
-      attend_tile<D, NQB, 1>(kB, vB, qf, o, m, l, scale_log2, L - (p0 + wave + 4 * (i + 1)) * PAGE, G, lane);
-      if (i + 3 < npw) { const size_t t = tile_base(i + 3); load_kv_page<D>(kc + t, vc + t, lane, kB, vB); }
-    }
-  }
-
-  // ---- the block's own rows (last split only), taken from k_new / v_new
   const uint16_t* __restrict__ kn_ = static_cast<const uint16_t*>(a.k_new);
   const uint16_t* __restrict__ vn_ = static_cast<const uint16_t*>(a.v_new);
+  const size_t tile = (size_t)PAGE * D;
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
-  const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
-  if (last && wave == ((p1 - p0) & 3)) {
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      kA[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
-                        : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      uint32_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * g + i;
-        h[i] = (t < R) ? vn_[blk + t * rstride + 16 * n + l16] : 0u;
+
+  int first = 1;
+  for (int cur = lo; cur < hi;) {
+    // the item (b, kvh) holding unit `cur`, and this workgroup's piece of it
+    const int b = find_request(pre, a.B, cur);
+    const int L = clamp_len(a, b);
+    const int ncp = (L + PAGE - 1) / PAGE, nfull = L / PAGE, u = ncp + 1;
+    const int kvh = (cur - pre[b]) / u;
+    const int istart = pre[b] + kvh * u;
+    const int seg_end = min(hi, istart + u);
+    const int unit0 = cur - istart, unit1 = seg_end - istart;
+    const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
+    const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
+
+    __syncthreads();  // the previous piece is done with qs and st_buf
+    // Q^T fragments (B operand of S^T = K Q^T): qs[qb][c][lane] = Q[row 16 qb + l16][32c + 8g ..]
+    for (int e = threadIdx.x; e < NQB * (D / 32) * 64; e += NT) {
+      const int ln = e & 63, c = (e >> 6) % (D / 32), qb = (e >> 6) / (D / 32);
+      const int qr = qb * 16 + (ln & 15);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qr < RG) {
+        const int r = qr / G, hg = qr - r * G;
+        v = *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D +
+                                            32 * c + 8 * (ln >> 4));
       }
-      vA[n][0] = h[0] | (h[1] << 16);
-      vA[n][1] = h[2] | (h[3] << 16);
+      qs[e] = v;
     }
-    attend_tile<D, NQB, 2>(kA, vA, qf, o, m, l, scale_log2, 0, G, lane);
-  }
-
-  // ---- merge the four waves in LDS: (w0 + w2) + (w1 + w3)
+    f32x4 o[QB][D / 16];
+    float m[QB], l[QB];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    l[qb] += __shfl_xor(l[qb], 16);
-    l[qb] += __shfl_xor(l[qb], 32);
-  }
-  __shared__ float sm[2][NQB * 64], sl[2][NQB * 64];
-  __shared__ float so[2][NQB * (D / 16) * 4 * 64];
-  if (wave >= 2) stash_state<D, NQB>(o, m, l, sm[wave - 2], sl[wave - 2], so[wave - 2], lane);
-  __syncthreads();
-  if (wave < 2) merge_state<D, NQB>(o, m, l, sm[wave], sl[wave], so[wave], lane);
-  __syncthreads();
-  if (wave == 1) stash_state<D, NQB>(o, m, l, sm[0], sl[0], so[0], lane);
-  __syncthreads();
+    for (int j = 0; j < QB; ++j) {
+      m[j] = neg_inf();
+      l[j] = 0.f;
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
 
-  // ---- append the block rows to their page slots (after every read of this split's pages)
-  if (last) {
+    // units unit0 + wg + 4i: full pages, then the partial page, then the block's rows.
+    // Page ids come 64 at a time, one per lane, read back as scalars.
+    u32x4 kf[D / 32];
+    u32x2 vf[D / 16];
+    const int full_end = min(unit1, nfull);
+    for (int c0 = unit0 + wg; c0 < full_end; c0 += 256) {
+      const int nu = min(64, (full_end - c0 + 3) / 4);
+      const int myu = c0 + 4 * lane;
+      const int my_id = (lane < nu) ? page_id(pt, myu, a.num_pages) : 0;
+      for (int i = 0; i < nu; ++i) {
+        const size_t t = ((size_t)__builtin_amdgcn_readlane(my_id, i) * Hkv + kvh) * tile;
+        load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
+        attend_tile<D, QB, 0>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+      }
+    }
+    // the partial page, if this piece holds it and it falls to this wave
+    if (nfull < ncp && unit0 <= nfull && nfull < unit1 && (nfull - unit0) % 4 == wg) {
+      const size_t t = ((size_t)page_id(pt, nfull, a.num_pages) * Hkv + kvh) * tile;
+      load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
+      attend_tile<D, QB, 1>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, L - nfull * PAGE, G, lane);
+    }
+    // the block's own rows (unit ncp), from k_new / v_new
+    if (unit0 <= ncp && ncp < unit1 && (ncp - unit0) % 4 == wg) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        kf[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) {
+        uint32_t h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int tok = 4 * g + t;
+          h[t] = (tok < R) ? vn_[blk + tok * rstride + 16 * n + l16] : 0u;
+        }
+        vf[n][0] = h[0] | (h[1] << 16);
+        vf[n][1] = h[2] | (h[3] << 16);
+      }
+      attend_tile<D, QB, 2>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, 0, G, lane);
+    }
+
+    // merge the four waves of each group, in the order ((w0 + w1) + w2) + w3
+#pragma unroll
+    for (int j = 0; j < QB; ++j) l[j] = row4_sum(l[j]);
+    float* buf = st_buf[grp];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      __syncthreads();
+      if (wg == ww) stash_state<D, QB>(o, m, l, buf, lane);
+      __syncthreads();
+      if (wg == 0) merge_state<D, QB>(o, m, l, buf, lane);
+    }
+
+    if (wg == 0) {
+      if (unit0 == 0 && unit1 == u) {
+        // the whole item is here: normalised output
+        uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          const int qr = (qb0 + j) * 16 + l16;
+          if (qr >= RG) continue;
+          const int r = qr / G, hg = qr - r * G;
+          const float inv = 1.f / l[j];
+          uint16_t* op = out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * g;
+#pragma unroll
+          for (int n = 0; n < D / 16; ++n) {
+            u32x2 wv;
+            wv[0] = cvt_pk_bf16(o[j][n][0] * inv, o[j][n][1] * inv);
+            wv[1] = cvt_pk_bf16(o[j][n][2] * inv, o[j][n][3] * inv);
+            *reinterpret_cast<u32x2*>(op + 16 * n) = wv;
+          }
+        }
+      } else {
+        // a piece: unnormalised state in slot (w, first piece ? 0 : 1)
+        const size_t slot = (size_t)w * 2 + (first ? 0 : 1);
+        float* po = a.part_o + slot * RG * D;
+        float* pml = a.part_ml + slot * RG * 2;
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          const int qr = (qb0 + j) * 16 + l16;
+          if (qr >= RG) continue;
+#pragma unroll
+          for (int n = 0; n < D / 16; ++n)
+            *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = o[j][n];
+          if (g == 0) {
+            pml[qr * 2] = m[j];
+            pml[qr * 2 + 1] = l[j];
+          }
+        }
+      }
+    }
+    first = 0;
+    cur = seg_end;
+  }
+}
+
+// After every read of the cache: merge the pieces of items that crossed workgroup
+// boundaries (in workgroup order) and write the block's K/V rows into their page slots.
+constexpr int COMBINE_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const AttnLaunch a, int W) {
+  __shared__ int pre[MAX_B + 1];
+  build_prefix(a, pre);
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
+  const int L = clamp_len(a, b);
+  const int u = units_of(L);
+  const int T = pre[a.B];
+  const int s0 = pre[b] + kvh * u, e0 = s0 + u;
+  const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
+  const size_t tile = (size_t)PAGE * D;
+  const size_t rstride = (size_t)Hkv * D;
+  const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
+
+  // append: K in 16-byte units of 8 dims, V element by element
+  {
     uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
     uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    // K: 16-byte units of 8 dims; V: single elements
-    for (int e = threadIdx.x; e < R * (D / 8); e += THREADS) {
+    const uint16_t* kn_ = static_cast<const uint16_t*>(a.k_new);
+    const uint16_t* vn_ = static_cast<const uint16_t*>(a.v_new);
+    for (int e = threadIdx.x; e < R * (D / 8); e += COMBINE_THREADS) {
       const int t = e / (D / 8), d8 = e - t * (D / 8);
       const int j = L + t;
       const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
       *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) =
           *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
     }
-    for (int e = threadIdx.x; e < R * D; e += THREADS) {
+    for (int e = threadIdx.x; e < R * D; e += COMBINE_THREADS) {
       const int t = e / D, d = e - t * D;
       const int j = L + t, slot = j % PAGE;
       const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] =
-          vn_[blk + t * rstride + d];
+      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] = vn_[blk + t * rstride + d];
     }
   }
 
-  if (wave != 0) return;
-  merge_state<D, NQB>(o, m, l, sm[0], sl[0], so[0], lane);
-  if (nsplit == 1) {
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qr = qb * 16 + l16;
-      if (qr >= RG) continue;
-      const int r = qr / G, hg = qr - r * G;
-      const float inv = 1.f / l[qb];
-      uint16_t* op = out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * g;
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n) {
-        u32x2 w;
-        w[0] = pack_bf16x2(o[qb][n][0] * inv, o[qb][n][1] * inv);
-        w[1] = pack_bf16x2(o[qb][n][2] * inv, o[qb][n][3] * inv);
-        *reinterpret_cast<u32x2*>(op + 16 * n) = w;
-      }
-    }
-  } else {
-    // unnormalised partial state of this split; the combine kernel merges them
-    const size_t slot = ((size_t)b * Hkv + kvh) * a.splits_max + s;
-    float* po = a.part_o + slot * RG * D;
-    float* pml = a.part_ml + slot * RG * 2;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qr = qb * 16 + l16;
-      if (qr >= RG) continue;
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n)
-        *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = o[qb][n];
-      if (g == 0) {
-        pml[qr * 2] = m[qb];
-        pml[qr * 2 + 1] = l[qb];
-      }
-    }
-  }
-}
-
-// Merge the split partials of one (request, KV head) in split order.  Only requests whose
-// cached pages span more than one split have work here.
-constexpr int COMBINE_BATCH = 8;
-
-template <int D>
-__global__ __launch_bounds__(THREADS) void attn_combine_kernel(const AttnLaunch a) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int L = min(max(a.ctx_lens[b], 0), a.max_ctx_len);
-  const int nsplit = split_count(L, a.pages_per_split);
-  if (nsplit <= 1) return;
-  const int R = a.R, G = a.G, Hq = a.Hq, RG = R * G;
-  const size_t slot0 = ((size_t)b * a.Hkv + kvh) * a.splits_max;
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int it = threadIdx.x; it < RG * (D / 4); it += THREADS) {
-    const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+  // workgroups whose ranges intersect [s0, e0)
+  int w0 = (int)(((long long)s0 * W) / T);
+  while (w0 + 1 < W && range_lo(w0 + 1, T, W) <= s0) ++w0;
+  while (w0 > 0 && range_lo(w0, T, W) > s0) --w0;
+  int w1 = w0;
+  while (w1 + 1 < W && range_lo(w1 + 1, T, W) < e0) ++w1;
+  if (w0 == w1) return;  // one workgroup held the whole item and wrote it
+  // piece k = workgroup w0 + k; its slot is 2w, except the first piece when the item
+  // starts after that workgroup's range start (then it was its second piece)
+  const int np = w1 - w0 + 1;
+  auto slot_of = [&](int k) -> int {
+    const int ww = w0 + k;
+    if (range_lo(ww, T, W) >= range_lo(ww + 1, T, W)) return -1;  // empty range
+    return 2 * ww + ((k == 0 && range_lo(ww, T, W) < s0) ? 1 : 0);
+  };
+  // phase 1: per query row, the pieces' overall maximum and normaliser
+  __shared__ float s_M[64], s_inv[64];
+  for (int qr = threadIdx.x; qr < RG; qr += COMBINE_THREADS) {
     float M = neg_inf();
-    for (int s0 = 0; s0 < nsplit; s0 += COMBINE_BATCH) {
-      float mv[COMBINE_BATCH];
-#pragma unroll
-      for (int k = 0; k < COMBINE_BATCH; ++k)
-        mv[k] = (s0 + k < nsplit) ? a.part_ml[((slot0 + s0 + k) * RG + qr) * 2] : neg_inf();
-#pragma unroll
-      for (int k = 0; k < COMBINE_BATCH; ++k) M = fmaxf(M, mv[k]);
+    for (int k = 0; k < np; ++k) {
+      const int sl = slot_of(k);
+      if (sl >= 0) M = fmaxf(M, a.part_ml[((size_t)sl * RG + qr) * 2]);
     }
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += COMBINE_BATCH) {
-      f32x4 ov[COMBINE_BATCH];
-      float mv[COMBINE_BATCH], lv[COMBINE_BATCH];
-#pragma unroll
-      for (int k = 0; k < COMBINE_BATCH; ++k) {
-        if (s0 + k < nsplit) {
-          const size_t sl = slot0 + s0 + k;
-          ov[k] = *reinterpret_cast<const f32x4*>(a.part_o + (sl * RG + qr) * D + 4 * d4);
-          mv[k] = a.part_ml[(sl * RG + qr) * 2];
-          lv[k] = a.part_ml[(sl * RG + qr) * 2 + 1];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < COMBINE_BATCH; ++k) {
-        if (s0 + k < nsplit) {
-          const float f = exp2_hw(mv[k] - M);
-          den += f * lv[k];
-          num += f * ov[k];
-        }
+    for (int k = 0; k < np; ++k) {
+      const int sl = slot_of(k);
+      if (sl >= 0) {
+        const float* ml = a.part_ml + ((size_t)sl * RG + qr) * 2;
+        den += exp2_hw(ml[0] - M) * ml[1];
       }
     }
-    const float inv = 1.f / den;
+    s_M[qr] = M;
+    s_inv[qr] = 1.f / den;
+  }
+  __syncthreads();
+  // phase 2: every output element is the weighted sum of its pieces, loaded in batches
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int it = threadIdx.x; it < RG * (D / 4); it += COMBINE_THREADS) {
+    const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+    const float M = s_M[qr];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < np; k0 += 4) {
+      f32x4 ov[4];
+      float mv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sl = (k0 + k < np) ? slot_of(k0 + k) : -1;
+        ov[k] = (sl >= 0) ? *reinterpret_cast<const f32x4*>(a.part_o + ((size_t)sl * RG + qr) * D + 4 * d4)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        mv[k] = (sl >= 0) ? a.part_ml[((size_t)sl * RG + qr) * 2] : neg_inf();
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += exp2_hw(mv[k] - M) * ov[k];
+    }
+    const float inv = s_inv[qr];
     const int r = qr / G, hg = qr - r * G;
-    u32x2 w;
-    w[0] = pack_bf16x2(num[0] * inv, num[1] * inv);
-    w[1] = pack_bf16x2(num[2] * inv, num[3] * inv);
-    *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = w;
+    u32x2 wv;
+    wv[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+    wv[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = wv;
   }
 }
 
@@ -466,31 +572,42 @@ __global__ __launch_bounds__(THREADS) void attn_f32_kernel(const AttnLaunch a) {
   }
 }
 
-template <int D>
-hipError_t launch_bf16(const AttnLaunch& a, hipStream_t s) {
-  const dim3 grid(a.splits_max, a.Hkv, a.B);
-  const int nqb = (a.R * a.G + 15) / 16;
-  switch (nqb) {
-    case 1: attn_bf16_kernel<D, 1><<<grid, THREADS, 0, s>>>(a); break;
-    case 2: attn_bf16_kernel<D, 2><<<grid, THREADS, 0, s>>>(a); break;
-    case 3: attn_bf16_kernel<D, 3><<<grid, THREADS, 0, s>>>(a); break;
-    case 4: attn_bf16_kernel<D, 4><<<grid, THREADS, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
+template <int D, int NQB>
+hipError_t launch_shape(const AttnLaunch& a, hipStream_t s) {
+  constexpr int NT = AttnShape<NQB>::THREADS;
+  // one workgroup per resident slot (every slot gets an equal share of tiles), fewer
+  // when the work is small
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, NQB>, NT, 0);
+  if (e != hipSuccess) return e;
+  const long long units_max = (long long)a.B * a.Hkv * ((a.max_ctx_len + PAGE - 1) / PAGE + 1);
+  long long W = (long long)max(1, per_cu) * max(1, cus);
+  if (const char* env = getenv("ISD_ATTN_WG")) {
+    const int v = atoi(env);
+    if (v >= 1) W = v;
   }
-  if (a.splits_max > 1) attn_combine_kernel<D><<<dim3(a.Hkv, a.B), THREADS, 0, s>>>(a);
+  W = std::min<long long>(W, std::max<long long>(1, (units_max + 15) / 16));
+  W = std::min<long long>(W, ATTN_MAX_WG);
+  attn_bf16_kernel<D, NQB><<<(int)W, NT, 0, s>>>(a);
+  attn_combine_kernel<D><<<dim3(a.Hkv, a.B), COMBINE_THREADS, 0, s>>>(a, (int)W);
   return hipGetLastError();
 }
 
-}  // namespace
-
-int attention_pages_per_split(int B, int Hkv, int max_ctx_len, int R) {
-  (void)B; (void)Hkv; (void)max_ctx_len; (void)R;
-  if (const char* e = getenv("ISD_ATTN_PPS")) {
-    const int v = atoi(e);
-    if (v >= 4 && v <= 4096) return v;
+template <int D>
+hipError_t launch_bf16(const AttnLaunch& a, hipStream_t s) {
+  switch ((a.R * a.G + 15) / 16) {
+    case 1: return launch_shape<D, 1>(a, s);
+    case 2: return launch_shape<D, 2>(a, s);
+    case 3: return launch_shape<D, 3>(a, s);
+    case 4: return launch_shape<D, 4>(a, s);
+    default: return hipErrorInvalidValue;
   }
-  return 32;
 }
+
+}  // namespace
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s) {
   if (a.dtype == 0) {

@@ -40,19 +40,16 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- attention workspace
 struct AttnWs {
-  int pps, splits_max;
   size_t part_o, part_ml, total;
 };
 
 AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
+  (void)B; (void)max_ctx_len;
   AttnWs w{};
   const int R = 2 * N - 1, G = Hq / Hkv, RG = R * G;
-  const int ncp = (max_ctx_len + ISD_PAGE_SIZE - 1) / ISD_PAGE_SIZE;
-  w.pps = isd::attention_pages_per_split(B, Hkv, max_ctx_len, R);
-  w.splits_max = ncp == 0 ? 1 : (ncp + w.pps - 1) / w.pps;
-  const size_t slots = (size_t)B * Hkv * w.splits_max;
+  const size_t slots = (size_t)isd::ATTN_MAX_WG * 2;
   w.part_o = 0;
-  w.part_ml = w.part_o + align256(slots * RG * D * sizeof(float));
+  w.part_ml = align256(slots * RG * D * sizeof(float));
   w.total = w.part_ml + align256(slots * RG * 2 * sizeof(float));
   return w;
 }
@@ -142,10 +139,14 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   if (!std::isfinite(scale)) return fail(ISD_ERR_INVALID_ARG, "attention: scale is not finite");
   if (dt == ISD_BF16 && R * G > 64)
     return fail(ISD_ERR_UNSUPPORTED, "attention: (2N-1)*Hq/Hkv = %d query rows per KV head (max 64)", R * G);
+  if (dt == ISD_BF16 && N > 8)
+    return fail(ISD_ERR_UNSUPPORTED, "attention: bf16 path takes N <= 8 (the block fits one 16-token tile)");
+  if (dt == ISD_BF16 && B > isd::ATTN_MAX_B)
+    return fail(ISD_ERR_UNSUPPORTED, "attention: bf16 path takes at most %d requests per call", isd::ATTN_MAX_B);
   if (dt == ISD_F32 && max_ctx_len + R > 16384)
     return fail(ISD_ERR_UNSUPPORTED, "attention: f32 path holds at most 16384 tokens");
   const AttnWs w = attn_ws(B, N, Hq, Hkv, D, max_ctx_len);
-  if (dt == ISD_BF16 && w.splits_max > 1 && (!workspace || workspace_bytes < w.total))
+  if (dt == ISD_BF16 && (!workspace || workspace_bytes < w.total))
     return fail(ISD_ERR_WORKSPACE, "attention: workspace %zu bytes, need %zu", workspace_bytes, w.total);
 
   isd::AttnLaunch a{};
@@ -154,7 +155,6 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   a.page_table = page_table; a.ctx_lens = ctx_lens; a.out = out;
   a.B = B; a.N = N; a.R = R; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.D = D;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages; a.max_ctx_len = max_ctx_len; a.scale = scale;
-  a.pages_per_split = w.pps; a.splits_max = w.splits_max;
   char* ws = static_cast<char*>(workspace);
   a.part_o = ws ? reinterpret_cast<float*>(ws + w.part_o) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(ws + w.part_ml) : nullptr;

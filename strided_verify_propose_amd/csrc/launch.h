@@ -23,14 +23,13 @@ struct AttnLaunch {
   int num_pages;
   int max_ctx_len;
   float scale;
-  int pages_per_split;   // cached pages handled by one workgroup (multiple of 4)
-  int splits_max;        // grid extent over splits
-  // workspace carve-up
-  float* part_o;         // [B*Hkv*splits_max][R*G][D]
-  float* part_ml;        // [B*Hkv*splits_max][R*G][2]
+  // workspace carve-up: two partial slots per workgroup of the balanced grid
+  float* part_o;         // [ATTN_MAX_WG * 2][R*G][D]
+  float* part_ml;        // [ATTN_MAX_WG * 2][R*G][2]
 };
+constexpr int ATTN_MAX_WG = 2048;  // workgroups of the balanced attention grid, at most
+constexpr int ATTN_MAX_B = 2048;   // requests per bf16 attention call
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
-int attention_pages_per_split(int B, int Hkv, int max_ctx_len, int R);
 
 // ---------------------------------------------------------------- verification
 constexpr int VCHUNK = 16384;   // vocab entries per stats workgroup

@@ -122,8 +122,8 @@ def test_proj_validation(L, kw, status):
 
 
 def test_workspace_queries_grow_with_shape(L):
-    small = L.isd_attention_workspace_bytes(2, 4, 32, 8, 128, 512)
-    big = L.isd_attention_workspace_bytes(64, 4, 32, 8, 128, 4096)
+    small = L.isd_attention_workspace_bytes(2, 2, 8, 8, 128, 512)      # 3 query rows per KV head
+    big = L.isd_attention_workspace_bytes(64, 4, 32, 8, 128, 4096)    # 28 query rows per KV head
     assert 0 < small < big
     assert L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 128) > \
         L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 0) > 0
