@@ -57,7 +57,7 @@ AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
 // ---------------------------------------------------------------- verify workspace
 struct VerWs {
   int RR, SV, NSUB;
-  size_t cmax, cidx, csub, ws, rsub, total;
+  size_t cmax, cref, cidx, csub, ws, rsub, total;
 };
 
 VerWs ver_ws(int B, int N, int V) {
@@ -67,7 +67,8 @@ VerWs ver_ws(int B, int N, int V) {
   w.NSUB = (V + isd::VSUB - 1) / isd::VSUB;
   const size_t rows = (size_t)B * w.RR;
   w.cmax = 0;
-  w.cidx = w.cmax + align256(rows * w.SV * sizeof(float));
+  w.cref = w.cmax + align256(rows * w.SV * sizeof(float));
+  w.cidx = w.cref + align256(rows * w.SV * sizeof(float));
   w.csub = w.cidx + align256(rows * w.SV * sizeof(int32_t));
   w.ws = w.csub + align256(rows * w.NSUB * sizeof(float));
   w.rsub = w.ws + align256((size_t)B * sizeof(isd::WalkState));
@@ -202,6 +203,7 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
   v.p_draft = p_draft; v.q_draft = q_draft; v.row_lse = row_lse;
   char* ws = static_cast<char*>(workspace);
   v.cmax = reinterpret_cast<float*>(ws + w.cmax);
+  v.cref = reinterpret_cast<float*>(ws + w.cref);
   v.cidx = reinterpret_cast<int32_t*>(ws + w.cidx);
   v.csub = reinterpret_cast<float*>(ws + w.csub);
   v.ws = reinterpret_cast<isd::WalkState*>(ws + w.ws);

@@ -40,8 +40,9 @@ struct WalkState {              // per request, written by the walk, read by the
   int rej;                      // first rejected draft index, -1 if none / handled in the walk
   int pad;
   double up;                    // (u - a) / (1 - a)
-  float mp, mq;                 // row maxima (raw logits) of p_{rej} and q~_{rej}
-  float izp_hi, izp_lo;         // 1/Z of p_{rej} in units of 2^((l - mp) * c2), split hi + lo
+  double zp;                    // Z of p_{rej} (units of 2^(l c2 - kp))
+  float kp, kq;                 // row references (max of the chunk references) of p_{rej}, q~_{rej}
+  float izp_hi, izp_lo;         // 1/Z of p_{rej}, split hi + lo
   float izq_hi, izq_lo;
 };
 
@@ -63,8 +64,9 @@ struct VerifyLaunch {
   float* row_lse;
   // workspace
   float* cmax;                  // [B][RR][SV]  chunk max of raw logits
+  float* cref;                  // [B][RR][SV]  chunk reference K = fp32(cmax * c2)
   int32_t* cidx;                // [B][RR][SV]  lowest index of the chunk max
-  float* csub;                  // [B][RR][NSUB] sum 2^((l - cmax)*c2) per sub-chunk
+  float* csub;                  // [B][RR][NSUB] sum 2^(l c2 - K) per sub-chunk
   WalkState* ws;                // [B]
   float* rsub;                  // [B][NSUB] residual mass per sub-chunk
 };

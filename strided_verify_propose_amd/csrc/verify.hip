@@ -6,14 +6,16 @@
 // "Inference & ISD").  Proposals are argmax ids (page 1 "實際部署：SGLang 整合").  On a
 // rejection the next token comes from the normalised residual max(0, p - q~).
 //
-// Kernels (all HBM-streaming, no MFMA: this is a reduction over the vocabulary):
+// Kernels (HBM-streaming reductions over the vocabulary; no MFMA):
 //   stats    grid (chunk, row, request): one 16384-entry chunk of one row per workgroup.
-//            Chunk max of the raw logits, the lowest id holding it, and for every
-//            1024-entry sub-chunk the sum of 2^((l - chunk max) * log2(e)/T) (fp32).
-//   walk     one workgroup per request: combines chunk statistics in fp64 (row max,
-//            log-sum-exp), runs the acceptance walk, and draws every inverse-CDF sample
-//            from the fp64 prefix over sub-chunk sums plus one re-read sub-chunk.
-//   residual grid (chunk, request), only for requests whose sampled draft was rejected:
+//            Chunk max M of the raw logits, the lowest id holding it, the chunk reference
+//            K = M log2(e)/T rounded to fp32, and for every 1024-entry sub-chunk the sum
+//            of 2^(l log2(e)/T - K).  K is used exactly everywhere downstream, so every
+//            element weight has one rounding (the fma's) and no chunk carries a bias.
+//   walk     one workgroup (8 waves) per request: row max, argmax and normaliser from
+//            the chunk statistics in fp64; the acceptance walk; each inverse-CDF draw
+//            from an fp64 prefix over sub-chunk sums plus one re-read sub-chunk.
+//   residual grid (chunk, request), requests whose sampled draft was rejected only:
 //            per sub-chunk sums of max(0, p - q~) over the two rows involved.
 //   locate   one wave per such request: prefix over those sums, re-read one sub-chunk.
 // Argmax drafts (no draft rows) need no residual pass: the residual is p with the draft
@@ -27,28 +29,31 @@ namespace isd {
 namespace {
 
 constexpr int THREADS = 256;
+constexpr int WALK_THREADS = 512;
+constexpr int WALK_WAVES = WALK_THREADS / 64;
 constexpr int MAX_RR = 22;    // 2N-1 + N-1 rows for N <= 8
 constexpr int MAX_SV = 64;    // vocab <= 2^20
 
 template <typename T> struct VecOf;
 template <> struct VecOf<uint16_t> { static constexpr int n = 8; };
 template <> struct VecOf<float> { static constexpr int n = 4; };
+template <typename T> constexpr int kRounds = VCHUNK / (THREADS * VecOf<T>::n);
 
 __device__ __forceinline__ float to_f(uint16_t h) { return bf16_to_f32(h); }
 __device__ __forceinline__ float to_f(float f) { return f; }
 
-// Weight of a logit relative to a reference (a chunk or row maximum), 2^((l - ref) c2),
-// c2 = log2(e)/T.  Every kernel computes element weights through this one function, so
+// Weight of a logit against a chunk reference K: 2^(l c2 - K), c2 = log2(e)/T, one
+// rounding (the fma).  Every kernel computes element weights through this function, so
 // a re-read element gets exactly the weight the stats pass summed.
-__device__ __forceinline__ float rel_weight(float l, float ref, float c2) {
-  return exp2_hw((l - ref) * c2);
+__device__ __forceinline__ float rel_weight(float l, float K, float c2) {
+  return exp2_hw(fmaf(l, c2, -K));
 }
 
-// Residual weight max(0, p - q~) in fp32; 1/Z is applied as a hi + lo pair so its
-// rounding does not bias p against q~.
+// Residual weight max(0, p - q~) in fp32 against each row's reference; 1/Z is applied as
+// a hi + lo pair so its rounding does not bias p against q~.
 __device__ __forceinline__ float residual_weight(float lp, float lq, const WalkState& st, float c2) {
-  const float ep = rel_weight(lp, st.mp, c2);
-  const float eq = rel_weight(lq, st.mq, c2);
+  const float ep = rel_weight(lp, st.kp, c2);
+  const float eq = rel_weight(lq, st.kq, c2);
   const float p = fmaf(ep, st.izp_hi, ep * st.izp_lo);
   const float q = fmaf(eq, st.izq_hi, eq * st.izq_lo);
   return fmaxf(0.f, p - q);
@@ -66,9 +71,8 @@ template <typename T, bool VEC>
 __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int V, int base, int tid,
                                            float (&x)[VCHUNK / THREADS]) {
   constexpr int VE = VecOf<T>::n;
-  constexpr int ROUNDS = VCHUNK / (THREADS * VE);
 #pragma unroll
-  for (int k = 0; k < ROUNDS; ++k) {
+  for (int k = 0; k < kRounds<T>; ++k) {
     const int e0 = base + k * THREADS * VE + tid * VE;
     if (VEC && e0 + VE <= V) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(row + e0);
@@ -90,28 +94,35 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int V, int
   }
 }
 
-// Per-round wave sums -> per sub-chunk sums, in a fixed order.
+// Per-thread round sums -> sub-chunk sums, in a fixed order: the round sums go to LDS,
+// then 16 lanes per sub-chunk add their consecutive share and reduce in their 16-lane group.
 template <typename T>
-__device__ __forceinline__ void write_sub_sums(const float (&rs)[VCHUNK / (THREADS * VecOf<T>::n)][4],
-                                               float* out, int chunk, int nsub, int tid) {
+__device__ __forceinline__ void sub_sums(const float (&s)[kRounds<T>], float* lds, float* out,
+                                         int chunk, int nsub, int tid) {
   constexpr int VE = VecOf<T>::n;
-  constexpr int SPR = THREADS * VE / VSUB;  // sub-chunks per round
-  constexpr int WPS = 4 / SPR;              // waves per sub-chunk
-  if (tid < VCHUNK_SUBS) {
-    const int k = tid / SPR, part = tid % SPR;
-    float s = 0.f;
+  constexpr int TPS = VSUB / VE;              // threads covering one sub-chunk in a round
+  constexpr int SPR = THREADS / TPS;          // sub-chunks per round
+  constexpr int PER = TPS / 16;               // round sums per lane
 #pragma unroll
-    for (int w = 0; w < WPS; ++w) s += rs[k][part * WPS + w];
-    const int sub = chunk * VCHUNK_SUBS + tid;
-    if (sub < nsub) out[sub] = s;
-  }
+  for (int k = 0; k < kRounds<T>; ++k) lds[k * THREADS + tid] = s[k];
+  __syncthreads();
+  const int j = tid >> 4, p = tid & 15;       // sub-chunk of this chunk, lane in its group
+  const float* src = lds + (j / SPR) * THREADS + (j % SPR) * TPS + p * PER;
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v += src[i];
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  const int sub = chunk * VCHUNK_SUBS + j;
+  if (p == 0 && sub < nsub) out[sub] = v;
 }
 
 // ---------------------------------------------------------------- stats pass
 template <typename T, bool VEC>
 __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
   constexpr int VE = VecOf<T>::n;
-  constexpr int ROUNDS = VCHUNK / (THREADS * VE);
   const int chunk = blockIdx.x, rr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = chunk * VCHUNK;
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
 
   __shared__ float red[4];
   __shared__ int redi[4];
-  __shared__ float rs[ROUNDS][4];
+  __shared__ float lds[kRounds<T> * THREADS];
   float mx = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < VCHUNK / THREADS; ++i) mx = fmaxf(mx, x[i]);
@@ -129,31 +140,32 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float K = M * v.c2;
 
   const bool proposal = rr >= v.N - 1 && rr < v.R;
-  int arg = INT_MAX;
   if (proposal) {
+    int arg = INT_MAX;
 #pragma unroll
-    for (int k = 0; k < ROUNDS; ++k)
+    for (int k = 0; k < kRounds<T>; ++k)
 #pragma unroll
       for (int j = 0; j < VE; ++j)
         if (x[k * VE + j] == M && arg == INT_MAX) arg = base + k * THREADS * VE + tid * VE + j;
     arg = wave_min_i(arg);
     if (lane == 0) redi[wave] = arg;
   }
+  float s[kRounds<T>];
 #pragma unroll
-  for (int k = 0; k < ROUNDS; ++k) {
-    float s = 0.f;
+  for (int k = 0; k < kRounds<T>; ++k) {
+    float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < VE; ++j) s += rel_weight(x[k * VE + j], M, v.c2);
-    s = wave_sum(s);
-    if (lane == 0) rs[k][wave] = s;
+    for (int j = 0; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
+    s[k] = acc;
   }
-  __syncthreads();
   const size_t rowid = (size_t)b * v.RR + rr;
-  write_sub_sums<T>(rs, v.csub + rowid * v.NSUB, chunk, v.NSUB, tid);
+  sub_sums<T>(s, lds, v.csub + rowid * v.NSUB, chunk, v.NSUB, tid);
   if (tid == 0) {
     v.cmax[rowid * v.SV + chunk] = M;
+    v.cref[rowid * v.SV + chunk] = K;
     v.cidx[rowid * v.SV + chunk] =
         proposal ? min(min(redi[0], redi[1]), min(redi[2], redi[3])) : INT_MAX;
   }
@@ -239,41 +251,39 @@ __device__ int find_elem(ElemW elw, int e0, int cnt, double pre, double target, 
     const unsigned long long has = __ballot(last >= 0);
     const int src = has ? 63 - __clzll((long long)has) : 0;
     ans = __shfl(last, src);
-    if (ans < 0) ans = e0;
   }
-  return ans;
+  return ans < 0 ? e0 : ans;
 }
 
-// Inverse-CDF draw from row rr (weights 2^((l - M) c2)), optionally with one id removed.
+// Inverse-CDF draw from row rr in units of 2^(l c2 - Kmax), optionally with one id removed.
 template <typename T>
-__device__ int sample_row(const VerifyLaunch& v, int b, int rr, float M, double target, int excl,
+__device__ int sample_row(const VerifyLaunch& v, int b, int rr, float Kmax, double target, int excl,
                           int lane) {
   const T* __restrict__ row = row_ptr<T>(v, b, rr);
   const size_t rowid = (size_t)b * v.RR + rr;
-  const float* __restrict__ cm = v.cmax + rowid * v.SV;
+  const float* __restrict__ cr = v.cref + rowid * v.SV;
   const float* __restrict__ cs = v.csub + rowid * v.NSUB;
-  const double c2 = v.c2;
   double wex = 0.0;
   int exsub = -1;
   if (excl >= 0) {
     const int c = excl / VCHUNK;
-    wex = (double)rel_weight(to_f(row[excl]), cm[c], v.c2) * exp2((double)(cm[c] - M) * c2);
+    wex = (double)rel_weight(to_f(row[excl]), cr[c], v.c2) * exp2((double)cr[c] - (double)Kmax);
     exsub = excl / VSUB;
   }
   auto subw = [&](int j) -> double {
     const int c = j / VCHUNK_SUBS;
-    double w = (double)cs[j] * exp2((double)(cm[c] - M) * c2);
+    double w = (double)cs[j] * exp2((double)cr[c] - (double)Kmax);
     if (j == exsub) w = fmax(0.0, w - wex);
     return w;
   };
   double pre;
   const int js = find_sub(subw, v.NSUB, target, lane, pre);
   const int c = js / VCHUNK_SUBS;
-  const float ref = cm[c];
-  const double fc = exp2((double)(ref - M) * c2);
+  const float Kc = cr[c];
+  const double fc = exp2((double)Kc - (double)Kmax);
   auto elw = [&](int k) -> double {
     if (k == excl) return 0.0;
-    return (double)rel_weight(to_f(row[k]), ref, v.c2) * fc;
+    return (double)rel_weight(to_f(row[k]), Kc, v.c2) * fc;
   };
   const int e0 = js * VSUB;
   return find_elem(elw, e0, min(VSUB, v.V - e0), pre, target, lane);
@@ -281,62 +291,75 @@ __device__ int sample_row(const VerifyLaunch& v, int b, int rr, float M, double 
 
 // ---------------------------------------------------------------- walk
 template <typename T>
-__global__ __launch_bounds__(THREADS) void walk_kernel(const VerifyLaunch v) {
+__global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = v.N, R = v.R, RR = v.RR, SV = v.SV, NSUB = v.NSUB;
-  const double c2 = v.c2;
-  __shared__ float s_M[MAX_RR];
+  const T* lg = static_cast<const T*>(v.logits);
+  const T* dl = static_cast<const T*>(v.draft);
+  __shared__ float s_M[MAX_RR], s_K[MAX_RR];
   __shared__ int s_arg[MAX_RR];
   __shared__ double s_Z[MAX_RR];
+  __shared__ float s_lp[8], s_lq[8];
   __shared__ int s_rej;
   __shared__ double s_a, s_u;
 
-  // A. per row: max, argmax, Z = sum_k 2^((l_k - M) c2) (fp64 over chunk factors)
-  for (int rr = wave; rr < RR; rr += 4) {
+  // logits at the draft ids, gathered in parallel
+  if (tid < N - 1) {
+    const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + tid], 0), v.V - 1);
+    s_lp[tid] = to_f(lg[((size_t)b * R + tid) * v.V + d]);
+  } else if (dl && tid >= 64 && tid < 64 + N - 1) {
+    const int i = tid - 64;
+    const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + i], 0), v.V - 1);
+    s_lq[i] = to_f(dl[((size_t)b * (N - 1) + i) * v.V + d]);
+  }
+
+  // A. per row (one wave each): raw max and its lowest id, reference Kmax, and
+  //    Z = sum_k 2^(l_k c2 - Kmax) over the sub-chunk sums (fp64)
+  for (int rr = wave; rr < RR; rr += WALK_WAVES) {
     const size_t rowid = (size_t)b * RR + rr;
     const float* cm = v.cmax + rowid * SV;
+    const float* cr = v.cref + rowid * SV;
     const int32_t* ci = v.cidx + rowid * SV;
     const float* cs = v.csub + rowid * NSUB;
-    float M = -__builtin_inff();
-    for (int c = lane; c < SV; c += 64) M = fmaxf(M, cm[c]);
-    M = wave_max(M);
-    int arg = INT_MAX;
-    for (int c = lane; c < SV; c += 64)
-      if (cm[c] == M) arg = min(arg, ci[c]);
-    arg = wave_min_i(arg);
+    const float mv = (lane < SV) ? cm[lane] : -__builtin_inff();
+    const float kv = (lane < SV) ? cr[lane] : -__builtin_inff();
+    const int iv = (lane < SV) ? ci[lane] : INT_MAX;
+    const float M = wave_max(mv);
+    const float Kmax = wave_max(kv);
+    const int arg = wave_min_i(mv == M ? iv : INT_MAX);
+    // chunk factors 2^(K_c - Kmax), one per lane, then shared by shuffles
+    const double fl = (lane < SV) ? exp2((double)kv - (double)Kmax) : 0.0;
     double z = 0.0;
-    for (int j = lane; j < NSUB; j += 64)
-      z += (double)cs[j] * exp2((double)(cm[j / VCHUNK_SUBS] - M) * c2);
+    for (int j0 = 0; j0 < NSUB; j0 += 64) {
+      const int j = j0 + lane;
+      const double f = __shfl(fl, min(j, NSUB - 1) / VCHUNK_SUBS);
+      if (j < NSUB) z += (double)cs[j] * f;
+    }
     z = wave_sum_d(z);
     if (lane == 0) {
       s_M[rr] = M;
+      s_K[rr] = Kmax;
       s_arg[rr] = arg;
       s_Z[rr] = z;
     }
   }
   __syncthreads();
 
-  // B. the acceptance walk (one thread)
+  // B. the acceptance walk (one thread; everything it needs is in LDS)
   if (tid == 0) {
-    const T* lg = static_cast<const T*>(v.logits);
-    const T* dl = static_cast<const T*>(v.draft);
+    const double c2 = v.c2;
+    const double ln2 = 0.6931471805599453;
     if (v.row_lse) {
       for (int rr = 0; rr < R + N - 1; ++rr)
         v.row_lse[(size_t)b * (R + N - 1) + rr] =
-            (rr < RR) ? (float)((double)s_M[rr] * v.invT + log(s_Z[rr])) : 0.f;
+            (rr < RR) ? (float)(((double)s_K[rr] + log2(s_Z[rr])) * ln2) : 0.f;
     }
     int rej = -1;
     double ra = 1.0, ru = 0.0;
     for (int i = 0; i < N - 1; ++i) {
-      const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + i], 0), v.V - 1);
-      const float lp = to_f(lg[((size_t)b * R + i) * v.V + d]);
-      const double P = exp2(((double)lp - s_M[i]) * c2) / s_Z[i];
-      double Q = 1.0;
-      if (dl) {
-        const float lq = to_f(dl[((size_t)b * (N - 1) + i) * v.V + d]);
-        Q = exp2(((double)lq - s_M[R + i]) * c2) / s_Z[R + i];
-      }
+      const double P = exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
+      const double Q = dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
       if (v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
       if (v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
       const double a = (P >= Q) ? 1.0 : P / Q;
@@ -361,13 +384,15 @@ __global__ __launch_bounds__(THREADS) void walk_kernel(const VerifyLaunch v) {
     st.rej = -1;
     st.pad = 0;
     st.up = 0.0;
-    st.mp = st.mq = 0.f;
+    st.zp = 1.0;
+    st.kp = st.kq = 0.f;
     st.izp_hi = st.izp_lo = st.izq_hi = st.izq_lo = 0.f;
     if (rej >= 0 && dl) {
       st.rej = rej;
       st.up = (ru - ra) / (1.0 - ra);
-      st.mp = s_M[rej];
-      st.mq = s_M[R + rej];
+      st.zp = s_Z[rej];
+      st.kp = s_K[rej];
+      st.kq = s_K[R + rej];
       const double izp = 1.0 / s_Z[rej], izq = 1.0 / s_Z[R + rej];
       st.izp_hi = (float)izp;
       st.izp_lo = (float)(izp - (double)st.izp_hi);
@@ -378,16 +403,16 @@ __global__ __launch_bounds__(THREADS) void walk_kernel(const VerifyLaunch v) {
   }
   __syncthreads();
 
-  // C. inverse-CDF draws: N proposal rows, plus the argmax-draft residual
+  // C. inverse-CDF draws, one wave each: N proposal rows, plus the argmax-draft residual
   const int rej = s_rej;
-  const bool argmax_residual = (rej >= 0) && (v.draft == nullptr);
+  const bool argmax_residual = (rej >= 0) && (dl == nullptr);
   const int jobs = N + (argmax_residual ? 1 : 0);
-  for (int jb = wave; jb < jobs; jb += 4) {
+  for (int jb = wave; jb < jobs; jb += WALK_WAVES) {
     int k;
     if (jb < N) {
       const int rr = N - 1 + jb;
       const double u = (double)v.u[(size_t)b * R + rr];
-      k = sample_row<T>(v, b, rr, s_M[rr], u * s_Z[rr], -1, lane);
+      k = sample_row<T>(v, b, rr, s_K[rr], u * s_Z[rr], -1, lane);
       if (lane == 0) {
         v.sampled_ids[(size_t)b * N + jb] = k;
         v.argmax_ids[(size_t)b * N + jb] = s_arg[rr];
@@ -397,17 +422,17 @@ __global__ __launch_bounds__(THREADS) void walk_kernel(const VerifyLaunch v) {
       // residual of a one-hot q~: p_rej with the draft removed, drawn at (u - a)/(1 - a)
       const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + rej], 0), v.V - 1);
       const T* row = row_ptr<T>(v, b, rej);
-      const float* cm = v.cmax + ((size_t)b * RR + rej) * SV;
-      const float M = s_M[rej];
+      const float* cr = v.cref + ((size_t)b * RR + rej) * SV;
+      const float Kmax = s_K[rej];
       const int c = d / VCHUNK;
-      const double wd = (double)rel_weight(to_f(row[d]), cm[c], v.c2) *
-                        exp2((double)(cm[c] - M) * c2);
+      const double wd = (double)rel_weight(to_f(row[d]), cr[c], v.c2) *
+                        exp2((double)cr[c] - (double)Kmax);
       const double W = s_Z[rej] - wd;
       const double up = (s_u - s_a) / (1.0 - s_a);
       if (W > 0.0)
-        k = sample_row<T>(v, b, rej, M, up * W, d, lane);
+        k = sample_row<T>(v, b, rej, Kmax, up * W, d, lane);
       else
-        k = sample_row<T>(v, b, rej, M, up * s_Z[rej], -1, lane);
+        k = sample_row<T>(v, b, rej, Kmax, up * s_Z[rej], -1, lane);
       if (lane == 0) v.next_token[b] = k;
     }
   }
@@ -417,26 +442,24 @@ __global__ __launch_bounds__(THREADS) void walk_kernel(const VerifyLaunch v) {
 template <typename T, bool VEC>
 __global__ __launch_bounds__(THREADS) void residual_kernel(const VerifyLaunch v) {
   constexpr int VE = VecOf<T>::n;
-  constexpr int ROUNDS = VCHUNK / (THREADS * VE);
   const int chunk = blockIdx.x, b = blockIdx.y;
   const WalkState st = v.ws[b];
   if (st.rej < 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int base = chunk * VCHUNK;
   float xp[VCHUNK / THREADS], xq[VCHUNK / THREADS];
   load_chunk<T, VEC>(row_ptr<T>(v, b, st.rej), v.V, base, tid, xp);
   load_chunk<T, VEC>(row_ptr<T>(v, b, v.R + st.rej), v.V, base, tid, xq);
-  __shared__ float rs[ROUNDS][4];
+  __shared__ float lds[kRounds<T> * THREADS];
+  float s[kRounds<T>];
 #pragma unroll
-  for (int k = 0; k < ROUNDS; ++k) {
-    float s = 0.f;
+  for (int k = 0; k < kRounds<T>; ++k) {
+    float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < VE; ++j) s += residual_weight(xp[k * VE + j], xq[k * VE + j], st, v.c2);
-    s = wave_sum(s);
-    if (lane == 0) rs[k][wave] = s;
+    for (int j = 0; j < VE; ++j) acc += residual_weight(xp[k * VE + j], xq[k * VE + j], st, v.c2);
+    s[k] = acc;
   }
-  __syncthreads();
-  write_sub_sums<T>(rs, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
+  sub_sums<T>(s, lds, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
 }
 
 template <typename T>
@@ -463,8 +486,7 @@ __global__ __launch_bounds__(64) void locate_kernel(const VerifyLaunch v) {
     k = find_elem(elw, e0, min(VSUB, v.V - e0), pre, target, lane);
   } else {
     // p <= q~ everywhere (only by rounding): draw from p itself
-    const double Zp = 1.0 / ((double)st.izp_hi + (double)st.izp_lo);
-    k = sample_row<T>(v, b, st.rej, st.mp, st.up * Zp, -1, lane);
+    k = sample_row<T>(v, b, st.rej, st.kp, st.up * st.zp, -1, lane);
   }
   if (lane == 0) v.next_token[b] = k;
 }
@@ -475,7 +497,7 @@ hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
   const dim3 g1(v.SV, v.RR, v.B);
   if (vec) stats_kernel<T, true><<<g1, THREADS, 0, s>>>(v);
   else stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
-  walk_kernel<T><<<v.B, THREADS, 0, s>>>(v);
+  walk_kernel<T><<<v.B, WALK_THREADS, 0, s>>>(v);
   if (v.draft) {
     const dim3 g3(v.SV, v.B);
     if (vec) residual_kernel<T, true><<<g3, THREADS, 0, s>>>(v);
