@@ -76,6 +76,7 @@ def main():
     import torch
 
     from strided_verify_propose_amd import isd, synth
+    from strided_verify_propose_amd.profsum import read_attention_traffic
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -96,8 +97,10 @@ def main():
              page_table=dt(att.page_table), ctx_lens=dt(att.ctx_lens))
     maxctx = int(att.ctx_lens.max())
     vsets = []
+    ver0 = None
     for k in range(args.verify_sets):
         v = synth.verify_inputs(scfg, seed=scfg.seed + 100 * k)
+        ver0 = v if ver0 is None else ver0
         vsets.append(dict(logits=dt(v.logits), draft_logits=dt(v.draft_logits),
                           draft_ids=dt(v.draft_ids), uniforms=dt(v.uniforms)))
     pin = synth.proj_inputs(pcfg)
@@ -152,7 +155,9 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
 
     a_bytes = attention_bytes(att.ctx_lens, scfg.R, scfg.Hq, scfg.Hkv, scfg.D)
+    # the attention step (its two kernels), timed with events on the launch stream
     a_us = float(np.mean(att_ms)) * 1e3
+    traffic = read_attention_traffic(os.path.join(ROOT, "profiles", f"attention_step_{scfg.name}_hbm.txt"))
     a_gbps = a_bytes / (a_us * 1e-6) / 1e9
     v_bytes = verify_bytes(scfg.B, N, scfg.V, int(rej.sum() / len(vsets)))
     v_us = float(np.mean(ver_ms)) * 1e3
@@ -197,50 +202,46 @@ def main():
                        "verify": round(v_us, 2)},
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
-        "roofline": {"bound": "hbm", "kernel": "attn_bf16_kernel (isd_attention_step)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "isd_attention_step (attn_bf16_kernel + attn_combine_kernel)",
                      "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": a_bytes},
         "input_generation_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(scfg, pcfg, att, pin)
+        line["cpu_baseline"] = cpu_baseline(scfg, att, ver0, pin)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(scfg, pcfg, att, pin, att_requests=4, ver_requests=8):
-    """The oracle, as it is, on a bounded sample of the same workload: the full projection,
-    attention for `att_requests` requests and verification for `ver_requests` requests,
-    scaled to one full 64-request step."""
+def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):
+    """The oracle, as it is, on the host cores: whole steps of the same workload (the
+    projection, attention for all requests, verification for all requests, on the first
+    verification input set), repeated until about `min_seconds` of CPU work."""
     from threadpoolctl import threadpool_info
 
     import oracle
-    from strided_verify_propose_amd import synth
-    t0 = time.perf_counter()
-    oracle.gated_lora_proj(pin.x, pin.w, pin.a, pin.b, pin.gate)
-    t_proj = time.perf_counter() - t0
-    bs = np.arange(att_requests)
-    t0 = time.perf_counter()
-    oracle.attention_step(att.q[bs], att.k_new[bs], att.v_new[bs], att.k_pages, att.v_pages,
-                          att.page_table[bs], att.ctx_lens[bs], att.scale)
-    t_att = (time.perf_counter() - t0) * float(np.sum(att.ctx_lens + scfg.R)) / \
-        float(np.sum(att.ctx_lens[bs] + scfg.R))
-    vc = synth.StepConfig(scfg.name, scfg.dtype, B=ver_requests, N=scfg.N, Hq=scfg.Hq,
-                          Hkv=scfg.Hkv, D=scfg.D, V=scfg.V, ctx=scfg.ctx, anchor_sd=scfg.anchor_sd,
-                          noise_sd=scfg.noise_sd, seed=scfg.seed)
-    v = synth.verify_inputs(vc)
-    t0 = time.perf_counter()
-    oracle.verify_step(v.logits, v.draft_logits, v.draft_ids, v.uniforms, scfg.N)
-    t_ver = (time.perf_counter() - t0) * scfg.B / ver_requests
-    step_s = t_proj + t_att + t_ver
+    t_proj = t_att = t_ver = 0.0
+    reps = 0
+    while reps == 0 or t_proj + t_att + t_ver < min_seconds:
+        t0 = time.perf_counter()
+        oracle.gated_lora_proj(pin.x, pin.w, pin.a, pin.b, pin.gate)
+        t1 = time.perf_counter()
+        oracle.attention_step(att.q, att.k_new, att.v_new, att.k_pages, att.v_pages,
+                              att.page_table, att.ctx_lens, att.scale)
+        t2 = time.perf_counter()
+        oracle.verify_step(ver.logits, ver.draft_logits, ver.draft_ids, ver.uniforms, scfg.N)
+        t3 = time.perf_counter()
+        t_proj, t_att, t_ver = t_proj + t1 - t0, t_att + t2 - t1, t_ver + t3 - t2
+        reps += 1
+    total = t_proj + t_att + t_ver
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": int(threads),
+    return {"value": round(reps / total, 4), "unit": "steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"full projection, attention for {att_requests} of {scfg.B} requests "
-                       f"(scaled by tokens), verification for {ver_requests} of {scfg.B} "
-                       f"requests (scaled by count); one step = {step_s:.1f} s"),
-            "seconds": {"proj": round(t_proj, 2), "attention_scaled": round(t_att, 2),
-                        "verify_scaled": round(t_ver, 2)}}
+            "sample": (f"{reps} whole step(s) of the benchmark workload ({scfg.B} requests: "
+                       f"projection, attention, verification), {total:.1f} s"),
+            "seconds_per_step": {"proj": round(t_proj / reps, 3), "attention": round(t_att / reps, 3),
+                                 "verify": round(t_ver / reps, 3)}}
 
 
 if __name__ == "__main__":

@@ -9,7 +9,8 @@
 //                rows -- and the tiles of A^T give T = bf16(X A).
 //   lora_kernel  gated rows only: Y = bf16(base + T B) with T B on MFMA (K = r).
 // Tiles: 64 x 128 per workgroup, 4 waves of 32 x 64 (2 x 4 MFMA 16x16x32 blocks), K in
-// steps of 64 through LDS with register prefetch of the next step.  Workgroups are
+// steps of 64: three steps of global loads in flight, one step staged in LDS, and the
+// next step's MFMA fragments read from LDS while the current step's MFMAs run.  Workgroups are
 // numbered so that the tiles sharing a weight-column block land on the same XCD and
 // reuse it from that XCD's L2.
 #include "device.h"
@@ -19,74 +20,135 @@ namespace isd {
 namespace {
 
 constexpr int BM = 64, BN = 128, BK = 64;
-constexpr int LDP = BK + 8;  // padded LDS row (elements)
 constexpr int THREADS = 256;
 constexpr int XCDS = 8;
+constexpr int PROJ_RING = 4;  // register stages of the load pipeline
+constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte loads per thread per k step
+constexpr int B_LOADS = BN * BK / 8 / THREADS;
 
-struct Tiles {
-  uint16_t a[BM][LDP];
-  uint16_t b[BN][LDP];
+// Barrier that orders LDS only.  A plain workgroup barrier also waits for every
+// outstanding global load, which would drain the load pipeline at every k step.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One k step (64) of operand data in flight for one thread.  Loads are row-contiguous:
+// eight consecutive lanes read one row's 128 bytes.
+struct Stage {
+  u32x4 a[A_LOADS];
+  u32x4 b[B_LOADS];
 };
 
-// Global -> registers: rows x 64 bf16 per operand tile, 16 B per thread per pass.
+// LDS tile of one operand: MFMA fragments [k half][16-row block][slot], 16 bytes per
+// slot.  Row r, 16-byte k chunk c (0..7) lives in fragment (c / 4, r / 16) at slot
+// (c % 4) * 16 + ((r % 16) ^ c).  The xor spreads the eight chunks of a row, written
+// by eight consecutive lanes, over all banks, and an MFMA operand read (lane l takes
+// slot l ^ c) stays one conflict-free 1 KB sweep.
 template <int ROWS>
-__device__ __forceinline__ void fetch(const uint16_t* __restrict__ src, int rows_valid, int ld,
-                                      int k, int tid, u32x4 (&r)[ROWS / 32]) {
+struct OpTile {
+  u32x4 f[2][ROWS / 16][64];
+};
+struct Tiles {
+  OpTile<BM> a;
+  OpTile<BN> b;
+};
+
+__device__ __forceinline__ int chunk_slot(int r, int c) { return (c & 3) * 16 + ((r & 15) ^ c); }
+
+__device__ __forceinline__ void issue(Stage& st, const uint16_t* const (&pa)[A_LOADS],
+                                      const uint16_t* const (&pb)[B_LOADS], int k) {
 #pragma unroll
-  for (int p = 0; p < ROWS / 32; ++p) {
-    const int idx = tid + THREADS * p;
-    const int row = idx >> 3, c8 = idx & 7;
-    r[p] = (row < rows_valid) ? *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + k + c8 * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int i = 0; i < A_LOADS; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(pa[i] + k);
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) st.b[i] = *reinterpret_cast<const u32x4*>(pb[i] + k);
 }
-template <int ROWS>
-__device__ __forceinline__ void stash(uint16_t (*dst)[LDP], int tid, const u32x4 (&r)[ROWS / 32]) {
+
+__device__ __forceinline__ void put(Tiles& t, const Stage& st, int tid) {
+  const int c = tid & 7;
 #pragma unroll
-  for (int p = 0; p < ROWS / 32; ++p) {
-    const int idx = tid + THREADS * p;
-    *reinterpret_cast<u32x4*>(&dst[idx >> 3][(idx & 7) * 8]) = r[p];
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    t.a.f[c >> 2][r >> 4][chunk_slot(r, c)] = st.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    t.b.f[c >> 2][r >> 4][chunk_slot(r, c)] = st.b[i];
   }
 }
 
-// acc(32 x 64 per wave) += A_tile * B_tile^T over one BK step.  Wave (wm, wn) owns rows
-// 32 wm .. and columns 64 wn ..
-__device__ __forceinline__ void mma_step(const Tiles& t, int wm, int wn, int lane,
-                                         f32x4 (&acc)[2][4]) {
-  const int l16 = lane & 15, g = lane >> 4;
+// MFMA operand fragments of one k step for this wave (rows 32 wm + 16 i, columns
+// 64 wn + 16 j), read from LDS one step ahead of their use.
+struct Frags {
+  u32x4 a[2][2];  // [k half][i]
+  u32x4 b[2][4];  // [k half][j]
+};
+
+__device__ __forceinline__ void fetch_frags(Frags& f, const Tiles& t, int wm, int wn, int lane) {
 #pragma unroll
-  for (int kk = 0; kk < BK / 32; ++kk) {
-    u32x4 af[2], bf[4];
+  for (int kk = 0; kk < 2; ++kk) {
+    const int slot = lane ^ (kk * 4 + (lane >> 4));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      af[i] = *reinterpret_cast<const u32x4*>(&t.a[wm * 32 + i * 16 + l16][kk * 32 + 8 * g]);
+    for (int i = 0; i < 2; ++i) f.a[kk][i] = t.a.f[kk][wm * 2 + i][slot];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(&t.b[wn * 64 + j * 16 + l16][kk * 32 + 8 * g]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+    for (int j = 0; j < 4; ++j) f.b[kk][j] = t.b.f[kk][wn * 4 + j][slot];
   }
 }
 
-// acc = sum over k in [0, K) of A[m0 + r, k] B[n0 + c, k]
-__device__ void gemm_tile(Tiles& t, const uint16_t* __restrict__ A, int lda, int mrows,
-                          const uint16_t* __restrict__ B, int ldb, int K, int tid, int wm, int wn,
+__device__ __forceinline__ void mma(const Frags& f, f32x4 (&acc)[2][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(f.a[kk][i], f.b[kk][j], acc[i][j]);
+}
+
+// acc = sum over k < K of X[row][k] Wt[col][k] for the 64 x 128 tile at X, Wt.  X rows
+// past `mrows` read row mrows - 1 (never stored).  Three pipelines overlap at step s:
+// global loads for step s + RING - 1 go out (RING register stages), step s + 2 goes from
+// registers to LDS, step s + 1's fragments come from LDS into registers, and step s's
+// MFMAs run on fragments already in registers.  LDS is double-buffered.
+template <int RING>
+__device__ void gemm_tile(Tiles (&lds)[2], const uint16_t* __restrict__ X, int ldx, int mrows,
+                          const uint16_t* __restrict__ Wt, int ldw, int K, int tid, int wm, int wn,
                           int lane, f32x4 (&acc)[2][4]) {
-  u32x4 ra[BM / 32], rb[BN / 32];
-  fetch<BM>(A, mrows, lda, 0, tid, ra);
-  fetch<BN>(B, BN, ldb, 0, tid, rb);
-  for (int k = 0; k < K; k += BK) {
-    __syncthreads();
-    stash<BM>(t.a, tid, ra);
-    stash<BN>(t.b, tid, rb);
-    __syncthreads();
-    if (k + BK < K) {
-      fetch<BM>(A, mrows, lda, k + BK, tid, ra);
-      fetch<BN>(B, BN, ldb, k + BK, tid, rb);
+  const uint16_t* pa[A_LOADS];
+  const uint16_t* pb[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i)
+    pa[i] = X + (size_t)min((tid >> 3) + 32 * i, mrows - 1) * ldx + (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) pb[i] = Wt + (size_t)((tid >> 3) + 32 * i) * ldw + (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  static_assert(RING % 2 == 0, "fragment buffers alternate with the step parity");
+  const int S = K / BK;
+  Stage r[RING];
+  Frags f[2];
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) issue(r[u], pa, pb, min(u, S - 1) * BK);
+  put(lds[0], r[0], tid);
+  put(lds[1], r[1], tid);
+  lds_barrier();
+  fetch_frags(f[0], lds[0], wm, wn, lane);
+  // Steps past the end re-load and re-stage the last step (unconditional loads keep the
+  // compiler's wait counts exact); only the MFMAs are skipped.
+  for (int s0 = 0; s0 < S; s0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int s = s0 + u;
+      issue(r[(u + RING - 1) % RING], pa, pb, min(s + RING - 1, S - 1) * BK);
+      fetch_frags(f[(u + 1) & 1], lds[(s + 1) & 1], wm, wn, lane);
+      put(lds[s & 1], r[(u + 2) % RING], tid);
+      if (s < S) mma(f[u & 1], acc);
+      lds_barrier();
     }
-    mma_step(t, wm, wn, lane, acc);
   }
 }
 
@@ -110,13 +172,9 @@ __global__ __launch_bounds__(THREADS) void base_kernel(const ProjLaunch p) {
   const int mrows = min(BM, p.M - m0);
   const bool lowrank = n0 >= p.Nout;  // this tile computes T = X A
   const uint16_t* Bsrc = lowrank ? p.A + (size_t)(n0 - p.Nout) * p.K : p.W + (size_t)n0 * p.K;
-  __shared__ Tiles t;
+  __shared__ Tiles lds[2];
   f32x4 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile(t, p.X + (size_t)m0 * p.K, p.K, mrows, Bsrc, p.K, p.K, tid, wm, wn, lane, acc);
+  gemm_tile<PROJ_RING>(lds, p.X + (size_t)m0 * p.K, p.K, mrows, Bsrc, p.K, p.K, tid, wm, wn, lane, acc);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -156,13 +214,9 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
   if (tid < mrows && p.gate[m0 + tid]) s_any = 1;
   __syncthreads();
   if (!s_any) return;
-  __shared__ Tiles t;
+  __shared__ Tiles lds[2];
   f32x4 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile(t, p.T + (size_t)m0 * p.r, p.r, mrows, p.Bl + (size_t)n0 * p.r, p.r, p.r, tid, wm, wn,
+  gemm_tile<PROJ_RING>(lds, p.T + (size_t)m0 * p.r, p.r, mrows, p.Bl + (size_t)n0 * p.r, p.r, p.r, tid, wm, wn,
             lane, acc);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
