@@ -43,7 +43,7 @@ def parse():
 
 
 def tpf_closed_form(N, p):
-    """Tokens per forward of ISD at acceptance rate p (page 5, "Speedup Factor Explorer")."""
+    """Tokens per forward of ISD at acceptance rate p (「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor Explorer")."""
     return (2 + sum(p ** k for k in range(1, N - 1))) / (2 - p ** (N - 1))
 
 

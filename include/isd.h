@@ -2,7 +2,7 @@
  *
  * One ISD decode step runs a block of 2N-1 query rows per request: N-1 rows verify the
  * previous step's proposals against the causal anchor distribution p, N [MASK] rows
- * propose new tokens (page 1 "I-DLM 如何解決這些問題"; page 3 "1. 引言"; page 5
+ * propose new tokens (「首次超越 AR 模型」 "I-DLM 如何解決這些問題"; 「内省扩散语言模型」 "1. 引言"; 「I-DLM – introspektive Diffusion Language Models」
  * "Inference & ISD").  The library provides the three data-parallel parts of that step:
  *
  *   isd_attention_step   strictly causal GQA attention of the block over a paged KV cache
@@ -59,10 +59,10 @@ const char* isd_last_error(void);
 
 /* ---------------------------------------------------------------- attention
  * Strictly causal GQA attention of the 2N-1 block rows over a paged KV cache.
- * Follows: the block of 2N-1 query positions per forward (page 1, section
+ * Follows: the block of 2N-1 query positions per forward (「首次超越 AR 模型」 section
  * "為什麼 I-DLM 能在高並發下保持高效"); strictly causal attention, which keeps the model
- * on an AR serving stack (page 1 "實際部署：SGLang 整合"; page 5 "I-DLM-Methodik"); a
- * paged KV cache read only through its pages (page 1 "實際部署：SGLang 整合"; page 5
+ * on an AR serving stack (「首次超越 AR 模型」 "實際部署：SGLang 整合"; 「I-DLM – introspektive Diffusion Language Models」 "I-DLM-Methodik"); a
+ * paged KV cache read only through its pages (「首次超越 AR 模型」 "實際部署：SGLang 整合"; 「I-DLM – introspektive Diffusion Language Models」
  * "Serving (SGLang)").
  *
  * R = 2N-1, G = Hq/Hkv.  dtype ISD_BF16 or ISD_F32 for every tensor.
@@ -98,9 +98,9 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
 /* ---------------------------------------------------------------- verification
  * Vocab-wide verification of one ISD step.  Follows: proposals at [MASK] positions from
  * q and verification at clean positions against the anchor p with acceptance
- * min(1, p(x)/q(x)), which keeps the output distribution that of the AR model (page 1
- * "I-DLM 如何解決這些問題"; page 5 "Inference & ISD"); argmax proposals (page 1
- * "實際部署：SGLang 整合"; page 5 "Serving (SGLang)").  On a rejection the next token is
+ * min(1, p(x)/q(x)), which keeps the output distribution that of the AR model (「首次超越 AR 模型」
+ * "I-DLM 如何解決這些問題"; 「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD"); argmax proposals (「首次超越 AR 模型」
+ * "實際部署：SGLang 整合"; 「I-DLM – introspektive Diffusion Language Models」 "Serving (SGLang)").  On a rejection the next token is
  * drawn from the normalised residual max(0, p - q~), the completion that keeps that
  * guarantee (the pages do not print it).
  *
@@ -137,7 +137,7 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
 /* ---------------------------------------------------------------- R-ISD projection
  * Gated residual adaptation of one linear layer: the LoRA delta is applied only on gated
  * ([MASK]) rows and verify rows use the base weights alone, so they equal the base model's
- * output bit for bit (page 1 "無損 R-ISD"; page 3 "1. 引言"; page 5 "Lossless R-ISD").
+ * output bit for bit (「首次超越 AR 模型」 "無損 R-ISD"; 「内省扩散语言模型」 "1. 引言"; 「I-DLM – introspektive Diffusion Language Models」 "Lossless R-ISD").
  * bf16 only; fp32 accumulation.  Storage follows the linear-layer convention:
  *   x [M, K]; w [Nout, K] (= W^T); a [r, K] (= A^T); b [Nout, r] (= B^T); y [M, Nout]
  *   gate [M] uint8 in {0, 1}; NULL => base-only (a and b may then be NULL)

@@ -1,15 +1,15 @@
 """Oracle: attention of one ISD step over a paged KV cache.  (Test infrastructure.)
 
 What it follows:
-  * The block of one step holds 2N-1 query positions per request (page 1, section
+  * The block of one step holds 2N-1 query positions per request (「首次超越 AR 模型」 section
     "為什麼 I-DLM 能在高並發下保持高效": seven queries per forward at N=4).
   * Attention is strictly causal, which is what lets the model run on an AR serving
-    stack (page 1 "實際部署：SGLang 整合"; page 5 "I-DLM-Methodik", AR-kompatibles Serving).
+    stack (「首次超越 AR 模型」 "實際部署：SGLang 整合"; 「I-DLM – introspektive Diffusion Language Models」 "I-DLM-Methodik", AR-kompatibles Serving).
     Read as: row r of the block sees every cached token and block rows 0..r, itself
     included -- no bidirectional attention inside the block.
   * K/V live in a paged cache and the attention kernel reads them only through the
-    pages (page 1 "實際部署：SGLang 整合", paged KV cache and paged-only attention kernel;
-    page 5 "Serving (SGLang)").  So the block's K/V are first written to their slots,
+    pages (「首次超越 AR 模型」 "實際部署：SGLang 整合", paged KV cache and paged-only attention kernel;
+    「I-DLM – introspektive Diffusion Language Models」 "Serving (SGLang)").  So the block's K/V are first written to their slots,
     then every key is gathered through the page table.
   * GQA: query head h reads KV head floor(h / (Hq/Hkv)); scale 1/sqrt(D); Q and K
     arrive after any positional transform.  (Head counts come from the Qwen3 shapes.)

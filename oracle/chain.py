@@ -1,10 +1,10 @@
 """Oracle: tokens per forward (TPF) of ISD.  (Test infrastructure.)
 
 What it follows:
-  * Page 5, "Speedup Factor Explorer": in the memory-bound regime the speedup is about
+  * 「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor Explorer": in the memory-bound regime the speedup is about
     TPF, given (with its exponents lost in extraction) as (2+p+...+p^(N-2)) / (2-p^(N-1)),
     and R-ISD's lossless speedup is about TPF / alpha.
-  * Page 1 "為什麼 I-DLM 能在高並發下保持高效" and page 5 "Durchsatz (Throughput)":
+  * 「首次超越 AR 模型」 "為什麼 I-DLM 能在高並發下保持高效" and 「I-DLM – introspektive Diffusion Language Models」 "Durchsatz (Throughput)":
     compute efficiency is TPF^2 / query count, with 2N-1 queries per forward for ISD.
 
 The closed form is what a two-state chain gives, which `simulate_chain` runs:

@@ -3,8 +3,8 @@
 What it follows:
   * R-ISD adds a gated LoRA adapter that is active only at [MASK] positions; verify
     positions use the base weights alone, so their outputs are those of the base AR
-    model bit for bit (page 1 "無損 R-ISD"; page 3 "1. 引言", gated residual
-    adaptation; page 5 "Speedup Factor Explorer" and "Lossless R-ISD").  Rank 128.
+    model bit for bit (「首次超越 AR 模型」 "無損 R-ISD"; 「内省扩散语言模型」 "1. 引言", gated residual
+    adaptation; 「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor Explorer" and "Lossless R-ISD").  Rank 128.
   * No LoRA scaling factor is given: the delta is added with scale 1, and the low-rank
     product X A is taken in the operand type of the second contraction (bf16).
 

@@ -3,16 +3,16 @@
 What it follows:
   * One forward both proposes and verifies: [MASK] positions propose new tokens from a
     proposal distribution q, clean ("introspective") positions re-check earlier tokens
-    against the causal anchor distribution p (page 1 "I-DLM 如何解決這些問題"; page 3
-    "1. 引言", contribution list; page 5 "Inference & ISD").
+    against the causal anchor distribution p (「首次超越 AR 模型」 "I-DLM 如何解決這些問題"; 「内省扩散语言模型」
+    "1. 引言", contribution list; 「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD").
   * A proposal x is accepted with probability min(1, p(x)/q(x)), which makes the emitted
-    tokens follow the AR distribution (page 1 "I-DLM 如何解決這些問題"; page 5
+    tokens follow the AR distribution (「首次超越 AR 模型」 "I-DLM 如何解決這些問題"; 「I-DLM – introspektive Diffusion Language Models」
     "Inference & ISD").  The pages do not print what happens on a rejection; the only
     completion that keeps that guarantee is the standard one, resampling from the
     normalised residual max(0, p - q) -- taken as the reading here.
-  * Proposals are argmax ids of the proposal rows (page 1 "實際部署：SGLang 整合",
-    argmax proposal; page 5 "Serving (SGLang)").
-  * Temperature divides the logits (the pages' example request uses 1.0, page 1 "快速開始").
+  * Proposals are argmax ids of the proposal rows (「首次超越 AR 模型」 "實際部署：SGLang 整合",
+    argmax proposal; 「I-DLM – introspektive Diffusion Language Models」 "Serving (SGLang)").
+  * Temperature divides the logits (the pages' example request uses 1.0, 「首次超越 AR 模型」 "快速開始").
 
 Layout of one request's rows: logits rows 0..N-2 are the anchors p_i that verify draft
 d_i; rows N-1..2N-2 are the N proposal rows.  draft_logits row i is the distribution

@@ -1,8 +1,8 @@
 // Strictly causal GQA attention of the 2N-1 strided block rows over a paged KV cache.
 //
-// Method (page 1 "為什麼 I-DLM 能在高並發下保持高效": 2N-1 queries per forward; page 1
-// "實際部署：SGLang 整合" and page 5 "I-DLM-Methodik": strictly causal attention; page 1
-// "實際部署：SGLang 整合" / page 5 "Serving (SGLang)": paged KV cache, paged-only kernel):
+// Method (「首次超越 AR 模型」 "為什麼 I-DLM 能在高並發下保持高效": 2N-1 queries per forward; 「首次超越 AR 模型」
+// "實際部署：SGLang 整合" and 「I-DLM – introspektive Diffusion Language Models」 "I-DLM-Methodik": strictly causal attention; 「首次超越 AR 模型」
+// "實際部署：SGLang 整合" / 「I-DLM – introspektive Diffusion Language Models」 "Serving (SGLang)": paged KV cache, paged-only kernel):
 //   out[b,r,h] = softmax_j(scale q[b,r,h].k_j) v_j over tokens j <= ctx_len[b] + r.
 //
 // bf16 kernel, one workgroup per (request b, KV head, split of cached pages):

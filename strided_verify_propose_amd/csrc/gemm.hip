@@ -1,6 +1,6 @@
 // R-ISD gated projection on gfx950 MFMA:  Y = X W + gate * bf16(X A) B   (bf16 in/out).
 //
-// R-ISD (page 1 "無損 R-ISD"; page 3 "1. 引言"; page 5 "Lossless R-ISD"): the LoRA
+// R-ISD (「首次超越 AR 模型」 "無損 R-ISD"; 「内省扩散语言模型」 "1. 引言"; 「I-DLM – introspektive Diffusion Language Models」 "Lossless R-ISD"): the LoRA
 // delta is added only on gated ([MASK]) rows; verify rows keep the base product bit
 // for bit.  Two kernels, no workgroup ever waits on another:
 //   base_kernel  one GEMM over the stacked weights [W^T; A^T] (Nout + r rows of K):

@@ -2,8 +2,8 @@
 //
 // Method: [MASK] rows propose from q, clean rows verify earlier proposals against the
 // causal anchor p, and a proposal x is kept with probability min(1, p(x)/q(x)), which
-// leaves the AR distribution unchanged (page 1 "I-DLM 如何解決這些問題"; page 5
-// "Inference & ISD").  Proposals are argmax ids (page 1 "實際部署：SGLang 整合").  On a
+// leaves the AR distribution unchanged (「首次超越 AR 模型」 "I-DLM 如何解決這些問題"; 「I-DLM – introspektive Diffusion Language Models」
+// "Inference & ISD").  Proposals are argmax ids (「首次超越 AR 模型」 "實際部署：SGLang 整合").  On a
 // rejection the next token comes from the normalised residual max(0, p - q~).
 //
 // Kernels (HBM-streaming reductions over the vocabulary; no MFMA):

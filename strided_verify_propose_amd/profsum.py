@@ -23,10 +23,15 @@ COPY_BYTES = 1 << 30
 
 
 def attention_source_hash() -> str:
+    """SHA-256 of the attention sources with comments and blank lines removed, so that a
+    change of wording does not invalidate the counters but any change of code does."""
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

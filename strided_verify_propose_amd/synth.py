@@ -8,9 +8,9 @@ Gumbel-max trick (argmax of logits plus Gumbel noise), which samples softmax(log
 exactly without normalising anything.
 
 Workload shapes follow the pages' model family: Qwen3-8B / Qwen3-32B attention shapes
-(page 1 "模型生態與安裝", page 5 "Model Zoo"), stride N=4 giving 2N-1 = 7 query rows
-(page 1 "為什麼 I-DLM 能在高並發下保持高效"), concurrency 64 (page 1 "吞吐量與並發性能"),
-bf16 (page 1 "快速開始").  Distributions are synthetic stand-ins for real prompts.
+(「首次超越 AR 模型」 "模型生態與安裝", 「I-DLM – introspektive Diffusion Language Models」 "Model Zoo"), stride N=4 giving 2N-1 = 7 query rows
+(「首次超越 AR 模型」 "為什麼 I-DLM 能在高並發下保持高效"), concurrency 64 (「首次超越 AR 模型」 "吞吐量與並發性能"),
+bf16 (「首次超越 AR 模型」 "快速開始").  Distributions are synthetic stand-ins for real prompts.
 """
 from __future__ import annotations
 
