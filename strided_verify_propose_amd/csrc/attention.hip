@@ -5,7 +5,7 @@
 // "實際部署：SGLang 整合" / 「I-DLM – introspektive Diffusion Language Models」 "Serving (SGLang)": paged KV cache, paged-only kernel):
 //   out[b,r,h] = softmax_j(scale q[b,r,h].k_j) v_j over tokens j <= ctx_len[b] + r.
 //
-// bf16 kernel, one workgroup per (request b, KV head, split of cached pages):
+// bf16 kernel: a resident grid of workgroups over a flattened work list.
 //   * The G query heads sharing a KV head and the R block rows form R*G query rows,
 //     handled as 16-row MFMA blocks, so every K/V byte read serves all of them.
 //   * Page layout is chosen for the MFMA operands: a K page [D/8][16][8] loads, one
@@ -14,19 +14,18 @@
 //     straight into the A operand of O^T = V^T P^T (16x16x16 bf16).  S^T's accumulator
 //     layout is exactly P^T's B-operand layout, and O^T keeps one query row per lane,
 //     so the online softmax needs no data movement except a 4-lane max.
-//   * The 4 waves take interleaved pages and software-prefetch the next one; their
-//     partial (max, sum, O) states merge in LDS in a fixed order.
-//   * The split holding the block also writes the block's K/V rows into their page
-//     slots (after its own page loop) and attends to them from registers with the
-//     causal mask.  No other workgroup reads those slots.
-//   * Work is balanced tile by tile: the (request, KV head, page) units are laid out in
-//     one list and every workgroup of a grid sized to the resident capacity takes an
-//     equal contiguous slice.  A workgroup writes the output of every item it holds whole,
-//     and an unnormalised partial (max, sum, O) for the at most two items cut by its slice
+//   * Work is balanced by estimated time: the (request, KV head) items and their 16-token
+//     tiles form one list in which every item also carries a fixed start-up cost, and
+//     every workgroup of a grid sized to the resident capacity takes an equal contiguous
+//     share.  A workgroup writes the output of every item it holds whole, and an
+//     unnormalised partial (max, sum, O) for the at most two items cut by its share's
 //     edges; a second kernel merges those in workgroup order and appends the block's K/V
 //     to the cache after all reads.  No workgroup waits on or signals another.
+//   * Inside a workgroup the four waves take the tiles of a piece round-robin (the
+//     block's own rows and the partial page first), keep the next page's loads in flight
+//     while using the current one, and merge their states through LDS in a fixed order,
+//     each wave combining and writing a quarter of the head dimension.
 #include <algorithm>
-#include <cstdlib>
 
 #include "device.h"
 #include "launch.h"
@@ -57,10 +56,11 @@ struct AttnShape {
 // One 16-token tile (a cached page or the block) against this wave's query blocks.
 // MODE 0: all tokens valid.  MODE 1: tokens t < nvalid valid.  MODE 2: block tile,
 // token t valid for query row q iff t <= q / G (causal, diagonal included).
-// Q^T fragments come from LDS: qs[qb][c][lane].
+// qf[j] holds the Q^T fragments (B operand) of query block qb0 + j; blocks from nqb on
+// do not exist.
 template <int D, int QB, int MODE>
 __device__ __forceinline__ void attend_tile(const u32x4 (&kf)[D / 32], u32x2 (&vf)[D / 16],
-                                            const u32x4* __restrict__ qs, int qb0, int nqb,
+                                            const u32x4 (&qf)[QB][D / 32], int qb0, int nqb,
                                             f32x4 (&o)[QB][D / 16], float (&m)[QB],
                                             float (&l)[QB], float scale_log2, int nvalid,
                                             int G, int lane) {
@@ -82,12 +82,9 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kf)[D / 32], u32x2 (&v
   for (int j = 0; j < QB; ++j) {
     const int qb = qb0 + j;
     if (qb >= nqb) break;
-    // keep each block's Q fragment reads next to their use (register pressure)
-    if (j > 0) __builtin_amdgcn_sched_barrier(0);
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      st = mfma16x16x32(kf[c], qs[(qb * (D / 32) + c) * 64 + lane], st);
+    for (int c = 0; c < D / 32; ++c) st = mfma16x16x32(kf[c], qf[j][c], st);
     // st[i] = S^T[token 4g+i][query row 16 qb + l16] (unscaled)
     if (MODE != 0) {
 #pragma unroll
@@ -131,7 +128,18 @@ __device__ __forceinline__ void load_kv_page(const uint16_t* kt, const uint16_t*
     vf[n] = *reinterpret_cast<const u32x2*>(vt + n * 256 + lane * 4);
 }
 
-// Wave state <-> LDS (one wave's worth), lane-contiguous so every access is conflict-free.
+// Barrier that orders LDS only.  A plain workgroup barrier also waits for every
+// outstanding global load and store of the waves, which would drain the page pipeline.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wave state (m, l, O) -> LDS, lane-contiguous so every access is conflict-free.
+template <int D, int QB>
+constexpr int state_floats() { return (2 * QB + QB * (D / 16) * 4) * 64; }
+
 template <int D, int QB>
 __device__ __forceinline__ void stash_state(const f32x4 (&o)[QB][D / 16], const float (&m)[QB],
                                             const float (&l)[QB], float* buf, int lane) {
@@ -145,48 +153,35 @@ __device__ __forceinline__ void stash_state(const f32x4 (&o)[QB][D / 16], const 
       for (int i = 0; i < 4; ++i) buf[(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane] = o[j][n][i];
   }
 }
-template <int D, int QB>
-__device__ __forceinline__ void merge_state(f32x4 (&o)[QB][D / 16], float (&m)[QB], float (&l)[QB],
-                                            const float* buf, int lane) {
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    const float mb = buf[(j * 2) * 64 + lane];
-    if (mb == neg_inf()) continue;
-    const float M = fmaxf(m[j], mb);
-    const float fa = (m[j] == neg_inf()) ? 0.f : exp2_hw(m[j] - M);
-    const float fb = exp2_hw(mb - M);
-    l[j] = fa * l[j] + fb * buf[(j * 2 + 1) * 64 + lane];
-    m[j] = M;
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[j][n][i] = fa * o[j][n][i] + fb * buf[(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane];
-  }
-}
 
 // ---------------------------------------------------------------- balanced work list
-// The flattened work list holds, for request b and KV head h, u_b = ceil(L_b/16) + 1
-// units: the cached pages in order, then the block's own rows.  Item (b, h) occupies
-// units [pre[b] + h u_b, pre[b] + (h+1) u_b) where pre is the exclusive prefix of Hkv u_b.
-// Workgroup w of a grid of W takes units [w T / W, (w+1) T / W): every workgroup gets the
-// same number of 16-token tiles, whatever the spread of context lengths.
-constexpr int MAX_B = 2048;  // requests per call on the bf16 path (prefix kept in LDS)
+// Item (b, h) -- request b, KV head h -- has u_b = ceil(L_b/16) + 1 units: the cached
+// pages, then the block's own rows.  Starting a piece of an item costs a few dependent
+// memory round trips, so the list charges every item ITEM_COST extra cost units ahead of
+// its real ones: item (b, h) covers cost [s, s + ITEM_COST + u_b) with
+// s = pre[b] + h (ITEM_COST + u_b), pre being the exclusive prefix of Hkv (ITEM_COST + u_b),
+// and its real units sit at [s + ITEM_COST, s + ITEM_COST + u_b).  Workgroup w of a grid
+// of W takes cost [w T / W, (w+1) T / W), so every workgroup gets the same estimated time
+// whatever the spread of context lengths and however many items its range touches.
+constexpr int MAX_B = 2048;    // requests per call on the bf16 path (prefix kept in LDS)
+constexpr int ITEM_COST = 24;  // start-up cost of a piece, in 16-token tiles
 
 __device__ __forceinline__ int units_of(int L) { return (L + PAGE - 1) / PAGE + 1; }
+__device__ __forceinline__ int cost_of(int L) { return units_of(L) + ITEM_COST; }
 
 __device__ __forceinline__ int clamp_len(const AttnLaunch& a, int b) {
   return min(max(a.ctx_lens[b], 0), a.max_ctx_len);
 }
 
-// pre[0..B] in LDS (exclusive prefix of Hkv * u_b); wave 0 builds it.  Ends with a barrier.
+// pre[0..B] in LDS (exclusive prefix of Hkv * cost_of(L_b)); wave 0 builds it.  Ends
+// with a barrier.
 __device__ void build_prefix(const AttnLaunch& a, int* pre) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (a.B + 63) / 64;
     const int b0 = min(a.B, lane * per), b1 = min(a.B, b0 + per);
     int sum = 0;
-    for (int b = b0; b < b1; ++b) sum += a.Hkv * units_of(clamp_len(a, b));
+    for (int b = b0; b < b1; ++b) sum += a.Hkv * cost_of(clamp_len(a, b));
     int incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -196,7 +191,7 @@ __device__ void build_prefix(const AttnLaunch& a, int* pre) {
     int run = incl - sum;
     for (int b = b0; b < b1; ++b) {
       pre[b] = run;
-      run += a.Hkv * units_of(clamp_len(a, b));
+      run += a.Hkv * cost_of(clamp_len(a, b));
     }
     if (lane == 63) pre[a.B] = incl;
   }
@@ -218,15 +213,15 @@ __device__ __forceinline__ int range_lo(int w, int T, int W) {
 }
 
 template <int D, int NQB>
-__global__ __launch_bounds__(AttnShape<NQB>::THREADS, (AttnShape<NQB>::QB == 1) ? 4 : 3)
+__global__ __launch_bounds__(AttnShape<NQB>::THREADS, (AttnShape<NQB>::QB == 1) ? 3 : 2)
 void attn_bf16_kernel(const AttnLaunch a) {
   constexpr int QB = AttnShape<NQB>::QB;
   constexpr int GROUPS = AttnShape<NQB>::GROUPS;
-  constexpr int NT = AttnShape<NQB>::THREADS;
-  constexpr int STATE = (2 * QB + QB * (D / 16) * 4) * 64;  // floats per stashed wave state
+  constexpr int STATE = state_floats<D, QB>();
+  constexpr int NB = D / 16;           // 16-dim output blocks
+  constexpr int NPW = NB / 4;          // output blocks merged and written per wave
   __shared__ int pre[MAX_B + 1];
-  __shared__ u32x4 qs[NQB * (D / 32) * 64];
-  __shared__ float st_buf[GROUPS][STATE];
+  __shared__ float st_buf[GROUPS][4][STATE];
 
   build_prefix(a, pre);
   const int T = pre[a.B];
@@ -247,32 +242,50 @@ void attn_bf16_kernel(const AttnLaunch a) {
   const size_t tile = (size_t)PAGE * D;
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
 
-  int first = 1;
+  int first = 1;  // no piece processed yet (selects the partial-result slot)
   for (int cur = lo; cur < hi;) {
-    // the item (b, kvh) holding unit `cur`, and this workgroup's piece of it
+    // the item (b, kvh) holding cost position `cur`, and this workgroup's piece of it
     const int b = find_request(pre, a.B, cur);
     const int L = clamp_len(a, b);
     const int ncp = (L + PAGE - 1) / PAGE, nfull = L / PAGE, u = ncp + 1;
-    const int kvh = (cur - pre[b]) / u;
-    const int istart = pre[b] + kvh * u;
+    const int kvh = (cur - pre[b]) / (u + ITEM_COST);
+    const int istart = pre[b] + kvh * (u + ITEM_COST) + ITEM_COST;  // first real unit
     const int seg_end = min(hi, istart + u);
-    const int unit0 = cur - istart, unit1 = seg_end - istart;
+    const int unit0 = max(cur - istart, 0), unit1 = seg_end - istart;
+    cur = seg_end;
+    if (unit1 <= unit0) continue;  // the range covers only this item's start-up share
     const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
     const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
+    const size_t hoff = (size_t)kvh * tile;
+    auto page_off = [&](int id) -> size_t { return (size_t)id * Hkv * tile + hoff; };
 
-    __syncthreads();  // the previous piece is done with qs and st_buf
-    // Q^T fragments (B operand of S^T = K Q^T): qs[qb][c][lane] = Q[row 16 qb + l16][32c + 8g ..]
-    for (int e = threadIdx.x; e < NQB * (D / 32) * 64; e += NT) {
-      const int ln = e & 63, c = (e >> 6) % (D / 32), qb = (e >> 6) / (D / 32);
-      const int qr = qb * 16 + (ln & 15);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qr < RG) {
-        const int r = qr / G, hg = qr - r * G;
-        v = *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D +
-                                            32 * c + 8 * (ln >> 4));
-      }
-      qs[e] = v;
+    // The piece's units in a fixed order -- the block's own rows (unit ncp) and the
+    // partial page (unit nfull) first, then the full pages ascending -- dealt round-robin
+    // to the four waves, so that every wave holds the same number of tiles.
+    const bool has_block = unit0 <= ncp && ncp < unit1;
+    const bool has_partial = nfull < ncp && unit0 <= nfull && nfull < unit1;
+    const int nspecial = (has_block ? 1 : 0) + (has_partial ? 1 : 0);
+    const bool do_block = has_block && wg == 0;
+    const bool do_partial = has_partial && wg == (has_block ? 1 : 0);
+    const int fend = min(unit1, nfull);  // full pages of the piece: [unit0, fend)
+    int c0 = unit0 + (wg < nspecial ? wg + 4 - nspecial : wg - nspecial);  // this wave's first
+
+    // Issue first what needs no page id: Q^T fragments (B operand of S^T = K Q^T), the
+    // page ids of this wave's first 64 full pages, the partial page's id, the block rows.
+    u32x4 qf[QB][D / 32];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int qr = (qb0 + j) * 16 + l16;
+      const int r = qr / G, hg = qr - r * G;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        qf[j][c] = (qb0 + j < NQB && qr < RG)
+                       ? *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D +
+                                                         32 * c + 8 * g)
+                       : u32x4{0u, 0u, 0u, 0u};
     }
+    int my_id = (c0 + 4 * lane < fend) ? page_id(pt, c0 + 4 * lane, a.num_pages) : 0;
+
     f32x4 o[QB][D / 16];
     float m[QB], l[QB];
 #pragma unroll
@@ -282,35 +295,14 @@ void attn_bf16_kernel(const AttnLaunch a) {
 #pragma unroll
       for (int n = 0; n < D / 16; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
+    u32x4 kf[D / 32], kf2[D / 32];
+    u32x2 vf[D / 16], vf2[D / 16];
 
-    // units unit0 + wg + 4i: full pages, then the partial page, then the block's rows.
-    // Page ids come 64 at a time, one per lane, read back as scalars.
-    u32x4 kf[D / 32];
-    u32x2 vf[D / 16];
-    const int full_end = min(unit1, nfull);
-    for (int c0 = unit0 + wg; c0 < full_end; c0 += 256) {
-      const int nu = min(64, (full_end - c0 + 3) / 4);
-      const int myu = c0 + 4 * lane;
-      const int my_id = (lane < nu) ? page_id(pt, myu, a.num_pages) : 0;
-      for (int i = 0; i < nu; ++i) {
-        const size_t t = ((size_t)__builtin_amdgcn_readlane(my_id, i) * Hkv + kvh) * tile;
-        load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
-        attend_tile<D, QB, 0>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
-      }
-    }
-    // the partial page, if this piece holds it and it falls to this wave
-    if (nfull < ncp && unit0 <= nfull && nfull < unit1 && (nfull - unit0) % 4 == wg) {
-      const size_t t = ((size_t)page_id(pt, nfull, a.num_pages) * Hkv + kvh) * tile;
-      load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
-      attend_tile<D, QB, 1>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, L - nfull * PAGE, G, lane);
-    }
-    // the block's own rows (unit ncp), from k_new / v_new
-    if (unit0 <= ncp && ncp < unit1 && (ncp - unit0) % 4 == wg) {
+    if (do_block) {  // the block's own rows, from k_new / v_new
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        kf[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
-                          : u32x4{0u, 0u, 0u, 0u};
+        kf2[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
+                           : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int n = 0; n < D / 16; ++n) {
         uint32_t h[4];
@@ -319,64 +311,114 @@ void attn_bf16_kernel(const AttnLaunch a) {
           const int tok = 4 * g + t;
           h[t] = (tok < R) ? vn_[blk + tok * rstride + 16 * n + l16] : 0u;
         }
-        vf[n][0] = h[0] | (h[1] << 16);
-        vf[n][1] = h[2] | (h[3] << 16);
+        vf2[n][0] = h[0] | (h[1] << 16);
+        vf2[n][1] = h[2] | (h[3] << 16);
       }
-      attend_tile<D, QB, 2>(kf, vf, qs, qb0, NQB, o, m, l, scale_log2, 0, G, lane);
+    }
+    if (do_partial) {
+      const size_t t = page_off(page_id(pt, nfull, a.num_pages));
+      load_kv_page<D>(kc + t, vc + t, lane, kf2, vf2);
+    }
+    // the first full page goes out before the special tile is used
+    if (c0 < fend) {
+      const size_t t = page_off(__builtin_amdgcn_readlane(my_id, 0));
+      load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_block) attend_tile<D, QB, 2>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, 0, G, lane);
+    if (do_partial)
+      attend_tile<D, QB, 1>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, L - nfull * PAGE, G, lane);
+
+    // Full pages, 64 page ids at a time (one per lane, read back as scalars).  Two
+    // register buffers: the next page's loads are issued before the current page is
+    // used, and a scheduling barrier keeps them there.  Loads inside the loop are
+    // unconditional, so the compiler's wait counts stay exact (the tail is peeled).
+    for (; c0 < fend; c0 += 256) {
+      const int nu = min(64, (fend - c0 + 3) / 4);
+      size_t t;
+      if (c0 != unit0 + (wg < nspecial ? wg + 4 - nspecial : wg - nspecial)) {
+        t = page_off(__builtin_amdgcn_readlane(my_id, 0));
+        load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
+      }
+      int i = 0;
+      for (; i + 2 < nu; i += 2) {
+        t = page_off(__builtin_amdgcn_readlane(my_id, i + 1));
+        load_kv_page<D>(kc + t, vc + t, lane, kf2, vf2);
+        __builtin_amdgcn_sched_barrier(0);
+        attend_tile<D, QB, 0>(kf, vf, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+        t = page_off(__builtin_amdgcn_readlane(my_id, i + 2));
+        load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        attend_tile<D, QB, 0>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+      }
+      if (i + 1 < nu) {
+        t = page_off(__builtin_amdgcn_readlane(my_id, i + 1));
+        load_kv_page<D>(kc + t, vc + t, lane, kf2, vf2);
+        __builtin_amdgcn_sched_barrier(0);
+        attend_tile<D, QB, 0>(kf, vf, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+        attend_tile<D, QB, 0>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+      } else {
+        attend_tile<D, QB, 0>(kf, vf, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
+      }
+      if (c0 + 256 < fend) my_id = (c0 + 256 + 4 * lane < fend) ? page_id(pt, c0 + 256 + 4 * lane, a.num_pages) : 0;
     }
 
-    // merge the four waves of each group, in the order ((w0 + w1) + w2) + w3
+    // Merge the group's four wave states: all four go to LDS, then wave k of the group
+    // combines output blocks [k NPW, (k+1) NPW) of every query row over the waves in the
+    // order 0, 1, 2, 3, and writes them.
 #pragma unroll
     for (int j = 0; j < QB; ++j) l[j] = row4_sum(l[j]);
-    float* buf = st_buf[grp];
+    stash_state<D, QB>(o, m, l, st_buf[grp][wg], lane);
+    lds_barrier();
+    const bool whole = (unit0 == 0 && unit1 == u);
+    const size_t slot = (size_t)w * 2 + (first ? 0 : 1);
+    float* po = a.part_o + slot * RG * D;
+    float* pml = a.part_ml + slot * RG * 2;
+    uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
-      __syncthreads();
-      if (wg == ww) stash_state<D, QB>(o, m, l, buf, lane);
-      __syncthreads();
-      if (wg == 0) merge_state<D, QB>(o, m, l, buf, lane);
-    }
-
-    if (wg == 0) {
-      if (unit0 == 0 && unit1 == u) {
-        // the whole item is here: normalised output
-        uint16_t* out = static_cast<uint16_t*>(a.out);
+    for (int j = 0; j < QB; ++j) {
+      const int qr = (qb0 + j) * 16 + l16;
+      float mw[4], fw[4];
+      float M = neg_inf();
 #pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          const int qr = (qb0 + j) * 16 + l16;
-          if (qr >= RG) continue;
-          const int r = qr / G, hg = qr - r * G;
-          const float inv = 1.f / l[j];
-          uint16_t* op = out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * g;
+      for (int k = 0; k < 4; ++k) {
+        mw[k] = st_buf[grp][k][(j * 2) * 64 + lane];
+        M = fmaxf(M, mw[k]);
+      }
+      float Lsum = 0.f;
 #pragma unroll
-          for (int n = 0; n < D / 16; ++n) {
-            u32x2 wv;
-            wv[0] = cvt_pk_bf16(o[j][n][0] * inv, o[j][n][1] * inv);
-            wv[1] = cvt_pk_bf16(o[j][n][2] * inv, o[j][n][3] * inv);
-            *reinterpret_cast<u32x2*>(op + 16 * n) = wv;
-          }
-        }
-      } else {
-        // a piece: unnormalised state in slot (w, first piece ? 0 : 1)
-        const size_t slot = (size_t)w * 2 + (first ? 0 : 1);
-        float* po = a.part_o + slot * RG * D;
-        float* pml = a.part_ml + slot * RG * 2;
+      for (int k = 0; k < 4; ++k) {
+        fw[k] = (mw[k] == neg_inf()) ? 0.f : exp2_hw(mw[k] - M);
+        Lsum += fw[k] * st_buf[grp][k][(j * 2 + 1) * 64 + lane];
+      }
+      const float inv = 1.f / Lsum;
+      const int r = qr / G, hg = qr - r * G;
 #pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          const int qr = (qb0 + j) * 16 + l16;
-          if (qr >= RG) continue;
+      for (int nn = 0; nn < NPW; ++nn) {
+        const int n = wg * NPW + nn;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int n = 0; n < D / 16; ++n)
-            *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = o[j][n];
-          if (g == 0) {
-            pml[qr * 2] = m[j];
-            pml[qr * 2 + 1] = l[j];
-          }
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i] += fw[k] * st_buf[grp][k][(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane];
+        if (qb0 + j >= NQB || qr >= RG) continue;
+        if (whole) {
+          u32x2 wv;
+          wv[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+          wv[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
+          *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 16 * n + 4 * g) = wv;
+        } else {
+          *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = acc;
         }
       }
+      if (!whole && wg == 0 && g == 0 && qb0 + j < NQB && qr < RG) {
+        pml[qr * 2] = M;
+        pml[qr * 2 + 1] = Lsum;
+      }
     }
+    lds_barrier();  // every wave has read the stashed states before they are overwritten
     first = 0;
-    cur = seg_end;
   }
 }
 
@@ -393,7 +435,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const Att
   const int L = clamp_len(a, b);
   const int u = units_of(L);
   const int T = pre[a.B];
-  const int s0 = pre[b] + kvh * u, e0 = s0 + u;
+  const int s = pre[b] + kvh * (u + ITEM_COST);  // the item's cost range starts here
+  const int s0 = s + ITEM_COST, e0 = s0 + u;      // and its real units here
   const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
   const size_t tile = (size_t)PAGE * D;
   const size_t rstride = (size_t)Hkv * D;
@@ -420,20 +463,21 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const Att
     }
   }
 
-  // workgroups whose ranges intersect [s0, e0)
+  // workgroups whose ranges intersect the real units [s0, e0)
   int w0 = (int)(((long long)s0 * W) / T);
   while (w0 + 1 < W && range_lo(w0 + 1, T, W) <= s0) ++w0;
   while (w0 > 0 && range_lo(w0, T, W) > s0) --w0;
   int w1 = w0;
   while (w1 + 1 < W && range_lo(w1 + 1, T, W) < e0) ++w1;
   if (w0 == w1) return;  // one workgroup held the whole item and wrote it
-  // piece k = workgroup w0 + k; its slot is 2w, except the first piece when the item
-  // starts after that workgroup's range start (then it was its second piece)
+  // piece k = workgroup w0 + k; its slot is 2w, except the first piece when that
+  // workgroup's range starts before this item (then it already held real units of an
+  // earlier item, and this is its second partial)
   const int np = w1 - w0 + 1;
   auto slot_of = [&](int k) -> int {
     const int ww = w0 + k;
     if (range_lo(ww, T, W) >= range_lo(ww + 1, T, W)) return -1;  // empty range
-    return 2 * ww + ((k == 0 && range_lo(ww, T, W) < s0) ? 1 : 0);
+    return 2 * ww + ((k == 0 && range_lo(ww, T, W) < s) ? 1 : 0);
   };
   // phase 1: per query row, the pieces' overall maximum and normaliser
   __shared__ float s_M[64], s_inv[64];
@@ -585,10 +629,6 @@ hipError_t launch_shape(const AttnLaunch& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const long long units_max = (long long)a.B * a.Hkv * ((a.max_ctx_len + PAGE - 1) / PAGE + 1);
   long long W = (long long)max(1, per_cu) * max(1, cus);
-  if (const char* env = getenv("ISD_ATTN_WG")) {
-    const int v = atoi(env);
-    if (v >= 1) W = v;
-  }
   W = std::min<long long>(W, std::max<long long>(1, (units_max + 15) / 16));
   W = std::min<long long>(W, ATTN_MAX_WG);
   attn_bf16_kernel<D, NQB><<<(int)W, NT, 0, s>>>(a);

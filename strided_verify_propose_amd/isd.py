@@ -94,9 +94,8 @@ _ws_cache: dict = {}
 
 
 def workspace(kind: str, nbytes: int, device, shape_key=()) -> torch.Tensor:
-    """Zero-filled device workspace, one per (entry point, device, shape arguments): the
-    library's completion counters return to zero after each call, but where they sit
-    depends on the shapes."""
+    """Device workspace, one per (entry point, device, shape arguments), kept for reuse.
+    The library does not depend on its contents on entry."""
     key = (kind, str(device), tuple(shape_key))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
