@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--verify-sets", type=int, default=3,
                     help="distinct seeded verification inputs rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager steps instead of HIP-graph replays of the same steps")
     ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
@@ -132,17 +134,48 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps, events around each call on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # ---- per-call times: eager steps with events around each call on the launch stream
+    n_ev = min(args.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
+    t_ev = time.perf_counter()
+    for i in range(n_ev):
         step(i, evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    eager_s = (time.perf_counter() - t_ev) / n_ev
     proj_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     att_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ver_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # ---- timed region: K whole steps.  One HIP graph per verification input set holds a
+    # whole step (the same launches as the eager step), so the steps run back to back
+    # without host launch gaps; --no-graph times the eager steps instead.
+    graphs = []
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for k in range(len(vsets)):
+                step(k)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for k in range(len(vsets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
 
     # ---- acceptance statistics from the kernel's own outputs
     n_acc = np.concatenate([vouts[k]["n_accept"].cpu().numpy() for k in range(len(vsets))])
@@ -207,6 +240,8 @@ def main():
                      "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": a_bytes},
+        "timing": ("hip graph replay of whole steps" if graphs else "eager launches"),
+        "eager_ms_per_step": round(1e3 * eager_s, 4),
         "input_generation_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:

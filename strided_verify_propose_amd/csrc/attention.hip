@@ -26,6 +26,7 @@
 //     while using the current one, and merge their states through LDS in a fixed order,
 //     each wave combining and writing a quarter of the head dimension.
 #include <algorithm>
+#include <atomic>
 
 #include "device.h"
 #include "launch.h"
@@ -620,15 +621,23 @@ template <int D, int NQB>
 hipError_t launch_shape(const AttnLaunch& a, hipStream_t s) {
   constexpr int NT = AttnShape<NQB>::THREADS;
   // one workgroup per resident slot (every slot gets an equal share of tiles), fewer
-  // when the work is small
-  int dev = 0, cus = 0, per_cu = 0;
+  // when the work is small; the slot count is queried once per device
+  static std::atomic<int> slots_of_device[64];
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, NQB>, NT, 0);
   if (e != hipSuccess) return e;
+  int slots = (dev >= 0 && dev < 64) ? slots_of_device[dev].load(std::memory_order_relaxed) : 0;
+  if (slots <= 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, NQB>, NT, 0);
+    if (e != hipSuccess) return e;
+    slots = max(1, per_cu) * max(1, cus);
+    if (dev >= 0 && dev < 64) slots_of_device[dev].store(slots, std::memory_order_relaxed);
+  }
   const long long units_max = (long long)a.B * a.Hkv * ((a.max_ctx_len + PAGE - 1) / PAGE + 1);
-  long long W = (long long)max(1, per_cu) * max(1, cus);
+  long long W = slots;
   W = std::min<long long>(W, std::max<long long>(1, (units_max + 15) / 16));
   W = std::min<long long>(W, ATTN_MAX_WG);
   attn_bf16_kernel<D, NQB><<<(int)W, NT, 0, s>>>(a);
