@@ -244,6 +244,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
 
   int first = 1;  // no piece processed yet (selects the partial-result slot)
+  int tag0 = -1, tag1 = -1;  // items whose partials went to slots 2w and 2w + 1
   for (int cur = lo; cur < hi;) {
     // the item (b, kvh) holding cost position `cur`, and this workgroup's piece of it
     const int b = find_request(pre, a.B, cur);
@@ -373,6 +374,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
     lds_barrier();
     const bool whole = (unit0 == 0 && unit1 == u);
     const size_t slot = (size_t)w * 2 + (first ? 0 : 1);
+    if (!whole) (first ? tag0 : tag1) = b * Hkv + kvh;
     float* po = a.part_o + slot * RG * D;
     float* pml = a.part_ml + slot * RG * 2;
     uint16_t* out = static_cast<uint16_t*>(a.out);
@@ -421,30 +423,42 @@ void attn_bf16_kernel(const AttnLaunch a) {
     lds_barrier();  // every wave has read the stashed states before they are overwritten
     first = 0;
   }
+  if (threadIdx.x == 0) {
+    a.part_tag[2 * w] = tag0;
+    a.part_tag[2 * w + 1] = tag1;
+  }
 }
 
-// After every read of the cache: merge the pieces of items that crossed workgroup
-// boundaries (in workgroup order) and write the block's K/V rows into their page slots.
+// After every read of the cache: write the block's K/V rows into their page slots and
+// merge the pieces of items that crossed workgroup boundaries.  The pieces of an item sit
+// in consecutive workgroups, so their slots are found by one scan of the slot tags and
+// merged in workgroup order.
 constexpr int COMBINE_THREADS = 256;
 
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const AttnLaunch a, int W) {
-  __shared__ int pre[MAX_B + 1];
-  build_prefix(a, pre);
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
-  const int L = clamp_len(a, b);
-  const int u = units_of(L);
-  const int T = pre[a.B];
-  const int s = pre[b] + kvh * (u + ITEM_COST);  // the item's cost range starts here
-  const int s0 = s + ITEM_COST, e0 = s0 + u;      // and its real units here
-  const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
-  const size_t tile = (size_t)PAGE * D;
-  const size_t rstride = (size_t)Hkv * D;
-  const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
+  const int item = b * a.Hkv + kvh;
+  const int R = a.R, G = a.G, Hq = a.Hq, RG = R * G;
+  __shared__ int s_lo, s_hi;
+  if (threadIdx.x == 0) {
+    s_lo = 2 * W;
+    s_hi = -1;
+  }
+  lds_barrier();
+  for (int t = threadIdx.x; t < 2 * W; t += COMBINE_THREADS)
+    if (a.part_tag[t] == item) {
+      atomicMin(&s_lo, t);
+      atomicMax(&s_hi, t);
+    }
 
   // append: K in 16-byte units of 8 dims, V element by element
   {
+    const int L = clamp_len(a, b), Hkv = a.Hkv;
+    const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
+    const size_t tile = (size_t)PAGE * D;
+    const size_t rstride = (size_t)Hkv * D;
+    const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
     uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
     uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
     const uint16_t* kn_ = static_cast<const uint16_t*>(a.k_new);
@@ -463,68 +477,120 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const Att
       vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] = vn_[blk + t * rstride + d];
     }
   }
-
-  // workgroups whose ranges intersect the real units [s0, e0)
-  int w0 = (int)(((long long)s0 * W) / T);
-  while (w0 + 1 < W && range_lo(w0 + 1, T, W) <= s0) ++w0;
-  while (w0 > 0 && range_lo(w0, T, W) > s0) --w0;
-  int w1 = w0;
-  while (w1 + 1 < W && range_lo(w1 + 1, T, W) < e0) ++w1;
-  if (w0 == w1) return;  // one workgroup held the whole item and wrote it
-  // piece k = workgroup w0 + k; its slot is 2w, except the first piece when that
-  // workgroup's range starts before this item (then it already held real units of an
-  // earlier item, and this is its second partial)
-  const int np = w1 - w0 + 1;
-  auto slot_of = [&](int k) -> int {
-    const int ww = w0 + k;
-    if (range_lo(ww, T, W) >= range_lo(ww + 1, T, W)) return -1;  // empty range
-    return 2 * ww + ((k == 0 && range_lo(ww, T, W) < s) ? 1 : 0);
-  };
-  // phase 1: per query row, the pieces' overall maximum and normaliser
-  __shared__ float s_M[64], s_inv[64];
-  for (int qr = threadIdx.x; qr < RG; qr += COMBINE_THREADS) {
-    float M = neg_inf();
-    for (int k = 0; k < np; ++k) {
-      const int sl = slot_of(k);
-      if (sl >= 0) M = fmaxf(M, a.part_ml[((size_t)sl * RG + qr) * 2]);
+  lds_barrier();  // s_lo, s_hi complete (the append stores need not be)
+  if (s_hi < 0) return;  // one workgroup held the whole item and wrote its output
+  // Piece k sits in workgroup w0 + k: the first piece in slot s_lo, the others in the
+  // first slot of their workgroup (their share starts inside this item); workgroups with
+  // empty shares hold none.  Wave 0 lists the slots in order.
+  __shared__ int s_slots[2 * ATTN_MAX_WG];
+  __shared__ int s_np;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int w0 = s_lo >> 1, nw = (s_hi >> 1) - w0 + 1;
+    int n = 0;
+    for (int k0 = 0; k0 < nw; k0 += 64) {
+      const int k = k0 + lane;
+      int sl = -1;
+      if (k < nw) sl = (k == 0) ? s_lo : 2 * (w0 + k);
+      const bool ok = sl >= 0 && a.part_tag[sl] == item;
+      const unsigned long long bal = __ballot(ok);
+      if (ok) s_slots[n + __popcll(bal & ((1ull << lane) - 1))] = sl;
+      n += __popcll(bal);
     }
+    if (lane == 0) s_np = n;
+  }
+  lds_barrier();
+  const int np = s_np;
+  auto slot_of = [&](int k) -> int { return s_slots[k]; };
+
+  // Per query row: the pieces' common maximum M and 1 / sum_k 2^(m_k - M) l_k.  Then every
+  // output element is sum_k 2^(m_k - M) O_k / den: the weights of up to CHUNK pieces at a
+  // time are staged in LDS, and the O loads of four elements and four pieces go out
+  // together.
+  constexpr int CHUNK = 32;                  // pieces staged in LDS at a time
+  constexpr int PER = 4;                     // elements per thread per pass
+  constexpr int KB = 4;                      // pieces per batch of loads
+  const int nitems = RG * (D / 4);           // output elements of 4 dims
+  __shared__ float s_m[CHUNK][64], s_l[CHUNK][64], s_f[CHUNK][64], s_M[64], s_inv[64];
+  if (np <= CHUNK) {
+    for (int idx = threadIdx.x; idx < np * 64; idx += COMBINE_THREADS) {
+      const int k = idx >> 6, qr = idx & 63;
+      if (qr < RG) {
+        const float* ml = a.part_ml + ((size_t)slot_of(k) * RG + qr) * 2;
+        s_m[k][qr] = ml[0];
+        s_l[k][qr] = ml[1];
+      }
+    }
+    lds_barrier();
+  }
+  for (int qr = threadIdx.x; qr < RG; qr += COMBINE_THREADS) {
+    auto m_of = [&](int k) -> float {
+      return np <= CHUNK ? s_m[k][qr] : a.part_ml[((size_t)slot_of(k) * RG + qr) * 2];
+    };
+    auto l_of = [&](int k) -> float {
+      return np <= CHUNK ? s_l[k][qr] : a.part_ml[((size_t)slot_of(k) * RG + qr) * 2 + 1];
+    };
+    float M = neg_inf();
+    for (int k = 0; k < np; ++k) M = fmaxf(M, m_of(k));
     float den = 0.f;
     for (int k = 0; k < np; ++k) {
-      const int sl = slot_of(k);
-      if (sl >= 0) {
-        const float* ml = a.part_ml + ((size_t)sl * RG + qr) * 2;
-        den += exp2_hw(ml[0] - M) * ml[1];
-      }
+      const float m = m_of(k);
+      den += ((m == neg_inf()) ? 0.f : exp2_hw(m - M)) * l_of(k);
     }
     s_M[qr] = M;
     s_inv[qr] = 1.f / den;
   }
-  __syncthreads();
-  // phase 2: every output element is the weighted sum of its pieces, loaded in batches
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int it = threadIdx.x; it < RG * (D / 4); it += COMBINE_THREADS) {
-    const int qr = it / (D / 4), d4 = it - qr * (D / 4);
-    const float M = s_M[qr];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < np; k0 += 4) {
-      f32x4 ov[4];
-      float mv[4];
+  for (int base = 0; base < nitems; base += PER * COMBINE_THREADS) {
+    f32x4 acc[PER];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int sl = (k0 + k < np) ? slot_of(k0 + k) : -1;
-        ov[k] = (sl >= 0) ? *reinterpret_cast<const f32x4*>(a.part_o + ((size_t)sl * RG + qr) * D + 4 * d4)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-        mv[k] = (sl >= 0) ? a.part_ml[((size_t)sl * RG + qr) * 2] : neg_inf();
+    for (int e = 0; e < PER; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < np; c0 += CHUNK) {
+      const int nk = min(CHUNK, np - c0);
+      const int nkp = (nk + KB - 1) / KB * KB;
+      lds_barrier();  // s_M ready; the previous chunk's weights are no longer read
+      for (int idx = threadIdx.x; idx < nkp * 64; idx += COMBINE_THREADS) {
+        const int k = idx >> 6, qr = idx & 63;
+        float f = 0.f;
+        if (k < nk && qr < RG) {
+          const float m = np <= CHUNK ? s_m[k][qr] : a.part_ml[((size_t)slot_of(c0 + k) * RG + qr) * 2];
+          f = (m == neg_inf()) ? 0.f : exp2_hw(m - s_M[qr]);
+        }
+        s_f[k][qr] = f;
       }
+      lds_barrier();
+      for (int k0 = 0; k0 < nkp; k0 += KB) {
+        f32x4 ov[PER][KB];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc += exp2_hw(mv[k] - M) * ov[k];
+        for (int e = 0; e < PER; ++e) {
+          const int it = min(base + e * COMBINE_THREADS + (int)threadIdx.x, nitems - 1);
+          const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+#pragma unroll
+          for (int k = 0; k < KB; ++k)
+            ov[e][k] = *reinterpret_cast<const f32x4*>(
+                a.part_o + ((size_t)slot_of(c0 + min(k0 + k, nk - 1)) * RG + qr) * D + 4 * d4);
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int it = min(base + e * COMBINE_THREADS + (int)threadIdx.x, nitems - 1);
+          const int qr = it / (D / 4);
+#pragma unroll
+          for (int k = 0; k < KB; ++k) acc[e] += s_f[k0 + k][qr] * ov[e][k];
+        }
+      }
     }
-    const float inv = s_inv[qr];
-    const int r = qr / G, hg = qr - r * G;
-    u32x2 wv;
-    wv[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
-    wv[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = wv;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int it = base + e * COMBINE_THREADS + threadIdx.x;
+      if (it >= nitems) break;
+      const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+      const float inv = s_inv[qr];
+      const int r = qr / G, hg = qr - r * G;
+      u32x2 wv;
+      wv[0] = cvt_pk_bf16(acc[e][0] * inv, acc[e][1] * inv);
+      wv[1] = cvt_pk_bf16(acc[e][2] * inv, acc[e][3] * inv);
+      *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = wv;
+    }
   }
 }
 
