@@ -22,6 +22,8 @@
 // removed, whose sub-chunk sums the stats pass already has.
 #include <limits.h>
 
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -168,6 +170,150 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
     v.cref[rowid * v.SV + chunk] = K;
     v.cidx[rowid * v.SV + chunk] =
         proposal ? min(min(redi[0], redi[1]), min(redi[2], redi[3])) : INT_MAX;
+  }
+}
+
+// Barrier that orders LDS only, so that loads already issued for the next chunk stay in
+// flight (a plain workgroup barrier waits for every outstanding load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The same statistics with 16-byte aligned rows, from a resident grid: workgroup w takes
+// the (row, chunk) units w, w + W, ... and keeps the next unit's loads in flight while it
+// reduces the current one.  Units are numbered (b RR + rr) SV + chunk.
+template <typename T>
+struct RawChunk {
+  u32x4 w[kRounds<T>];  // thread t, round k: 16 bytes at base + k THREADS VE + t VE
+};
+
+template <typename T>
+__device__ __forceinline__ void load_raw(const VerifyLaunch& v, int unit, int tid, RawChunk<T>& r) {
+  constexpr int VE = VecOf<T>::n;
+  const int rowid = unit / v.SV, chunk = unit - rowid * v.SV;
+  const int b = rowid / v.RR, rr = rowid - b * v.RR;
+  const T* __restrict__ row = row_ptr<T>(v, b, rr);
+  const int base = chunk * VCHUNK;
+#pragma unroll
+  for (int k = 0; k < kRounds<T>; ++k) {
+    const int e0 = base + k * THREADS * VE + tid * VE;
+    // past the row's end: load its first 16 bytes (in bounds), replaced by -inf below
+    r.w[k] = *reinterpret_cast<const u32x4*>(row + (e0 < v.V ? e0 : 0));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, int tid,
+                                              const RawChunk<T>& r, float* red, int* redi, float* lds) {
+  constexpr int VE = VecOf<T>::n;
+  constexpr int NE = VCHUNK / THREADS;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int rowid = unit / v.SV, chunk = unit - rowid * v.SV;
+  const int rr = rowid - (rowid / v.RR) * v.RR;
+  const int base = chunk * VCHUNK;
+  float x[NE];
+#pragma unroll
+  for (int k = 0; k < kRounds<T>; ++k) {
+    if constexpr (VE == 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[k * VE + 2 * i] = bf16_lo(r.w[k][i]);
+        x[k * VE + 2 * i + 1] = bf16_hi(r.w[k][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[k * VE + i] = __uint_as_float(r.w[k][i]);
+    }
+  }
+  if (base + VCHUNK > v.V) {  // the row's last chunk: entries past V read as -inf
+#pragma unroll
+    for (int k = 0; k < kRounds<T>; ++k)
+      if (base + k * THREADS * VE + tid * VE >= v.V)
+#pragma unroll
+        for (int j = 0; j < VE; ++j) x[k * VE + j] = -__builtin_inff();
+  }
+  float mloc = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < NE; ++i) mloc = fmaxf(mloc, x[i]);
+  const float mw = wave_max(mloc);
+  if (lane == 0) red[wave] = mw;
+  lds_barrier();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float K = M * v.c2;
+  const bool proposal = rr >= v.N - 1 && rr < v.R;
+  if (proposal) {
+    // lowest id holding M: only lanes whose own maximum is M look for it
+    int arg = INT_MAX;
+    if (mloc == M) {
+#pragma unroll
+      for (int k = kRounds<T> - 1; k >= 0; --k)
+#pragma unroll
+        for (int j = VE - 1; j >= 0; --j)
+          if (x[k * VE + j] == M) arg = base + k * THREADS * VE + tid * VE + j;
+    }
+    arg = wave_min_i(arg);
+    if (lane == 0) redi[wave] = arg;
+  }
+  float s[kRounds<T>];
+#pragma unroll
+  for (int k = 0; k < kRounds<T>; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
+    s[k] = acc;
+  }
+  // sub-chunk sums (as sub_sums, with an LDS-only barrier)
+  {
+    constexpr int TPS = VSUB / VE, SPR = THREADS / TPS, PER = TPS / 16;
+#pragma unroll
+    for (int k = 0; k < kRounds<T>; ++k) lds[k * THREADS + tid] = s[k];
+    lds_barrier();
+    const int j = tid >> 4, p = tid & 15;
+    const float* src = lds + (j / SPR) * THREADS + (j % SPR) * TPS + p * PER;
+    float vv = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) vv += src[i];
+    vv += __shfl_xor(vv, 8);
+    vv += __shfl_xor(vv, 4);
+    vv += __shfl_xor(vv, 2);
+    vv += __shfl_xor(vv, 1);
+    const int sub = chunk * VCHUNK_SUBS + j;
+    if (p == 0 && sub < v.NSUB) v.csub[(size_t)rowid * v.NSUB + sub] = vv;
+  }
+  if (tid == 0) {
+    v.cmax[(size_t)rowid * v.SV + chunk] = M;
+    v.cref[(size_t)rowid * v.SV + chunk] = K;
+    v.cidx[(size_t)rowid * v.SV + chunk] = proposal ? min(min(redi[0], redi[1]), min(redi[2], redi[3])) : INT_MAX;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(THREADS) void stats_resident_kernel(const VerifyLaunch v, int U) {
+  __shared__ float red[4];
+  __shared__ int redi[4];
+  __shared__ float lds[kRounds<T> * THREADS];
+  const int tid = threadIdx.x, W = gridDim.x, w = blockIdx.x;
+  const int n = (U - w + W - 1) / W;  // units of this workgroup (>= 1: W <= U)
+  RawChunk<T> ra, rb;
+  load_raw<T>(v, w, tid, ra);
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    load_raw<T>(v, w + (i + 1) * W, tid, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    stats_of_unit<T>(v, w + i * W, tid, ra, red, redi, lds);
+    load_raw<T>(v, w + (i + 2) * W, tid, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    stats_of_unit<T>(v, w + (i + 1) * W, tid, rb, red, redi, lds);
+  }
+  if (i + 1 < n) {
+    load_raw<T>(v, w + (i + 1) * W, tid, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    stats_of_unit<T>(v, w + i * W, tid, ra, red, redi, lds);
+    stats_of_unit<T>(v, w + (i + 1) * W, tid, rb, red, redi, lds);
+  } else {
+    stats_of_unit<T>(v, w + i * W, tid, ra, red, redi, lds);
   }
 }
 
@@ -495,8 +641,27 @@ template <typename T>
 hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
   const bool vec = ((size_t)v.V * sizeof(T)) % 16 == 0;
   const dim3 g1(v.SV, v.RR, v.B);
-  if (vec) stats_kernel<T, true><<<g1, THREADS, 0, s>>>(v);
-  else stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
+  if (vec) {
+    // a resident grid: a few workgroups per CU, each streaming its units
+    static std::atomic<int> slots_of_device[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int slots = (dev >= 0 && dev < 64) ? slots_of_device[dev].load(std::memory_order_relaxed) : 0;
+    if (slots <= 0) {
+      int cus = 0, per_cu = 0;
+      e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_resident_kernel<T>, THREADS, 0);
+      if (e != hipSuccess) return e;
+      slots = max(1, per_cu) * max(1, cus);
+      if (dev >= 0 && dev < 64) slots_of_device[dev].store(slots, std::memory_order_relaxed);
+    }
+    const int U = v.B * v.RR * v.SV;
+    stats_resident_kernel<T><<<min(U, slots), THREADS, 0, s>>>(v, U);
+  } else {
+    stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
+  }
   walk_kernel<T><<<v.B, WALK_THREADS, 0, s>>>(v);
   if (v.draft) {
     const dim3 g3(v.SV, v.B);
