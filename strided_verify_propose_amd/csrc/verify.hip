@@ -31,8 +31,6 @@ namespace isd {
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int WALK_THREADS = 512;
-constexpr int WALK_WAVES = WALK_THREADS / 64;
 constexpr int MAX_RR = 22;    // 2N-1 + N-1 rows for N <= 8
 constexpr int MAX_SV = 64;    // vocab <= 2^20
 
@@ -363,19 +361,39 @@ __device__ int find_sub(SubW subw, int nsub, double target, int lane, double& pr
   return jstar;
 }
 
-// Smallest entry k in [e0, e0 + cnt) with pre + prefix(e0..k) > target; lane l takes 16
-// consecutive entries.  Fallback: the last entry with positive weight.
-template <class ElemW>
-__device__ int find_elem(ElemW elw, int e0, int cnt, double pre, double target, int lane) {
+// Lane l's 16 consecutive entries k0 = e0 + 16 l .. k0 + 15 of a row (entries from
+// `end` on read as -inf); one or two 16-byte loads per lane when rows are 16-byte aligned.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load16(const T* __restrict__ row, int k0, int end, float (&x)[16]) {
+  constexpr int VE = VecOf<T>::n;
+  if (VEC && k0 + 16 <= end) {
+#pragma unroll
+    for (int q = 0; q < 16 / VE; ++q) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + k0 + q * VE);
+      if constexpr (VE == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[q * 8 + 2 * i] = bf16_lo(w[i]);
+          x[q * 8 + 2 * i + 1] = bf16_hi(w[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[q * 4 + i] = __uint_as_float(w[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = (k0 + t < end) ? to_f(row[k0 + t]) : -__builtin_inff();
+  }
+}
+
+// Smallest entry k = k0 + t (lane l holds k0 = e0 + 16 l with weights w16[t]) with
+// pre + prefix(e0..k) > target.  Fallback: the last entry with positive weight, else e0.
+__device__ int find_in16(const double (&w16)[16], int e0, double pre, double target, int lane) {
   const int k0 = e0 + lane * 16;
-  double w16[16];
   double s = 0.0;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int k = k0 + t;
-    w16[t] = (k < e0 + cnt) ? elw(k) : 0.0;
-    s += w16[t];
-  }
+  for (int t = 0; t < 16; ++t) s += w16[t];
   const double incl = wave_incl_scan_d(s, lane);
   const unsigned long long hit = __ballot(pre + incl > target);
   int ans = -1;
@@ -401,10 +419,11 @@ __device__ int find_elem(ElemW elw, int e0, int cnt, double pre, double target, 
   return ans < 0 ? e0 : ans;
 }
 
-// Inverse-CDF draw from row rr in units of 2^(l c2 - Kmax), optionally with one id removed.
-template <typename T>
-__device__ int sample_row(const VerifyLaunch& v, int b, int rr, float Kmax, double target, int excl,
-                          int lane) {
+// Inverse-CDF draw from row rr in units of 2^(l c2 - Kmax), optionally with one id
+// removed.  fac[c] = 2^(K_c - Kmax) for chunk c of this row.
+template <typename T, bool VEC>
+__device__ int sample_row(const VerifyLaunch& v, int b, int rr, const double* fac, double target,
+                          int excl, int lane) {
   const T* __restrict__ row = row_ptr<T>(v, b, rr);
   const size_t rowid = (size_t)b * v.RR + rr;
   const float* __restrict__ cr = v.cref + rowid * v.SV;
@@ -413,12 +432,11 @@ __device__ int sample_row(const VerifyLaunch& v, int b, int rr, float Kmax, doub
   int exsub = -1;
   if (excl >= 0) {
     const int c = excl / VCHUNK;
-    wex = (double)rel_weight(to_f(row[excl]), cr[c], v.c2) * exp2((double)cr[c] - (double)Kmax);
+    wex = (double)rel_weight(to_f(row[excl]), cr[c], v.c2) * fac[c];
     exsub = excl / VSUB;
   }
   auto subw = [&](int j) -> double {
-    const int c = j / VCHUNK_SUBS;
-    double w = (double)cs[j] * exp2((double)cr[c] - (double)Kmax);
+    double w = (double)cs[j] * fac[j / VCHUNK_SUBS];
     if (j == exsub) w = fmax(0.0, w - wex);
     return w;
   };
@@ -426,29 +444,42 @@ __device__ int sample_row(const VerifyLaunch& v, int b, int rr, float Kmax, doub
   const int js = find_sub(subw, v.NSUB, target, lane, pre);
   const int c = js / VCHUNK_SUBS;
   const float Kc = cr[c];
-  const double fc = exp2((double)Kc - (double)Kmax);
-  auto elw = [&](int k) -> double {
-    if (k == excl) return 0.0;
-    return (double)rel_weight(to_f(row[k]), Kc, v.c2) * fc;
-  };
-  const int e0 = js * VSUB;
-  return find_elem(elw, e0, min(VSUB, v.V - e0), pre, target, lane);
+  const double fc = fac[c];
+  const int e0 = js * VSUB, end = min(e0 + VSUB, v.V);
+  float x[16];
+  load16<T, VEC>(row, e0 + lane * 16, end, x);
+  double w16[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int k = e0 + lane * 16 + t;
+    w16[t] = (k < end && k != excl) ? (double)rel_weight(x[t], Kc, v.c2) * fc : 0.0;
+  }
+  return find_in16(w16, e0, pre, target, lane);
 }
 
-// ---------------------------------------------------------------- walk
-template <typename T>
-__global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v) {
-  const int b = blockIdx.x;
+// ---------------------------------------------------------------- walk + residual
+// Grid (chunks + 1, requests) with sampled drafts, (1, requests) with argmax drafts.  Every
+// workgroup takes its request's acceptance walk from the row statistics (a few KB, the same
+// arithmetic in each); the last workgroup of a request writes the walk's outputs and takes
+// the inverse-CDF draws, and with sampled drafts the others each sum their chunk of the
+// residual max(0, p - q~) of a rejecting request.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaunch v) {
+  constexpr int WAVES = THREADS / 64;
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const bool lead = chunk == (int)gridDim.x - 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = v.N, R = v.R, RR = v.RR, SV = v.SV, NSUB = v.NSUB;
   const T* lg = static_cast<const T*>(v.logits);
   const T* dl = static_cast<const T*>(v.draft);
-  __shared__ float s_M[MAX_RR], s_K[MAX_RR];
+  __shared__ float s_K[MAX_RR];
   __shared__ int s_arg[MAX_RR];
   __shared__ double s_Z[MAX_RR];
+  __shared__ double s_fac[MAX_RR][MAX_SV];
   __shared__ float s_lp[8], s_lq[8];
   __shared__ int s_rej;
   __shared__ double s_a, s_u;
+  __shared__ WalkState s_st;
 
   // logits at the draft ids, gathered in parallel
   if (tid < N - 1) {
@@ -460,9 +491,11 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
     s_lq[i] = to_f(dl[((size_t)b * (N - 1) + i) * v.V + d]);
   }
 
-  // A. per row (one wave each): raw max and its lowest id, reference Kmax, and
+  // A. per row (one wave each; the proposal rows only in the lead workgroup): raw max
+  //    and its lowest id, reference Kmax, chunk factors 2^(K_c - Kmax) and
   //    Z = sum_k 2^(l_k c2 - Kmax) over the sub-chunk sums (fp64)
-  for (int rr = wave; rr < RR; rr += WALK_WAVES) {
+  for (int rr = wave; rr < RR; rr += WAVES) {
+    if (!lead && rr >= N - 1 && rr < R) continue;
     const size_t rowid = (size_t)b * RR + rr;
     const float* cm = v.cmax + rowid * SV;
     const float* cr = v.cref + rowid * SV;
@@ -474,8 +507,8 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
     const float M = wave_max(mv);
     const float Kmax = wave_max(kv);
     const int arg = wave_min_i(mv == M ? iv : INT_MAX);
-    // chunk factors 2^(K_c - Kmax), one per lane, then shared by shuffles
     const double fl = (lane < SV) ? exp2((double)kv - (double)Kmax) : 0.0;
+    if (lane < SV) s_fac[rr][lane] = fl;
     double z = 0.0;
     for (int j0 = 0; j0 < NSUB; j0 += 64) {
       const int j = j0 + lane;
@@ -484,7 +517,6 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
     }
     z = wave_sum_d(z);
     if (lane == 0) {
-      s_M[rr] = M;
       s_K[rr] = Kmax;
       s_arg[rr] = arg;
       s_Z[rr] = z;
@@ -496,7 +528,7 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
   if (tid == 0) {
     const double c2 = v.c2;
     const double ln2 = 0.6931471805599453;
-    if (v.row_lse) {
+    if (lead && v.row_lse) {
       for (int rr = 0; rr < R + N - 1; ++rr)
         v.row_lse[(size_t)b * (R + N - 1) + rr] =
             (rr < RR) ? (float)(((double)s_K[rr] + log2(s_Z[rr])) * ln2) : 0.f;
@@ -506,8 +538,8 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
     for (int i = 0; i < N - 1; ++i) {
       const double P = exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
       const double Q = dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
-      if (v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
-      if (v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
+      if (lead && v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
+      if (lead && v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
       const double a = (P >= Q) ? 1.0 : P / Q;
       uint8_t acc = 0;
       if (rej < 0) {
@@ -520,9 +552,9 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
           ru = u;
         }
       }
-      v.accept[(size_t)b * (N - 1) + i] = acc;
+      if (lead) v.accept[(size_t)b * (N - 1) + i] = acc;
     }
-    v.n_accept[b] = (rej < 0) ? N - 1 : rej;
+    if (lead) v.n_accept[b] = (rej < 0) ? N - 1 : rej;
     s_rej = rej;
     s_a = ra;
     s_u = ru;
@@ -545,20 +577,43 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
       st.izq_hi = (float)izq;
       st.izq_lo = (float)(izq - (double)st.izq_hi);
     }
-    v.ws[b] = st;
+    s_st = st;
+    if (lead) v.ws[b] = st;
   }
   __syncthreads();
-
-  // C. inverse-CDF draws, one wave each: N proposal rows, plus the argmax-draft residual
   const int rej = s_rej;
+
+  if (!lead) {
+    // C. this chunk's residual sums of a rejecting request (sampled drafts)
+    const WalkState st = s_st;
+    if (st.rej < 0) return;
+    constexpr int VE = VecOf<T>::n;
+    const int base = chunk * VCHUNK;
+    float xp[VCHUNK / THREADS], xq[VCHUNK / THREADS];
+    load_chunk<T, VEC>(row_ptr<T>(v, b, st.rej), v.V, base, tid, xp);
+    load_chunk<T, VEC>(row_ptr<T>(v, b, v.R + st.rej), v.V, base, tid, xq);
+    __shared__ float lds[kRounds<T> * THREADS];
+    float sr[kRounds<T>];
+#pragma unroll
+    for (int k = 0; k < kRounds<T>; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < VE; ++j) acc += residual_weight(xp[k * VE + j], xq[k * VE + j], st, v.c2);
+      sr[k] = acc;
+    }
+    sub_sums<T>(sr, lds, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
+    return;
+  }
+
+  // D. inverse-CDF draws, one wave each: N proposal rows, plus the argmax-draft residual
   const bool argmax_residual = (rej >= 0) && (dl == nullptr);
   const int jobs = N + (argmax_residual ? 1 : 0);
-  for (int jb = wave; jb < jobs; jb += WALK_WAVES) {
+  for (int jb = wave; jb < jobs; jb += WAVES) {
     int k;
     if (jb < N) {
       const int rr = N - 1 + jb;
       const double u = (double)v.u[(size_t)b * R + rr];
-      k = sample_row<T>(v, b, rr, s_K[rr], u * s_Z[rr], -1, lane);
+      k = sample_row<T, VEC>(v, b, rr, s_fac[rr], u * s_Z[rr], -1, lane);
       if (lane == 0) {
         v.sampled_ids[(size_t)b * N + jb] = k;
         v.argmax_ids[(size_t)b * N + jb] = s_arg[rr];
@@ -569,46 +624,21 @@ __global__ __launch_bounds__(WALK_THREADS) void walk_kernel(const VerifyLaunch v
       const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + rej], 0), v.V - 1);
       const T* row = row_ptr<T>(v, b, rej);
       const float* cr = v.cref + ((size_t)b * RR + rej) * SV;
-      const float Kmax = s_K[rej];
       const int c = d / VCHUNK;
-      const double wd = (double)rel_weight(to_f(row[d]), cr[c], v.c2) *
-                        exp2((double)cr[c] - (double)Kmax);
+      const double wd = (double)rel_weight(to_f(row[d]), cr[c], v.c2) * s_fac[rej][c];
       const double W = s_Z[rej] - wd;
       const double up = (s_u - s_a) / (1.0 - s_a);
       if (W > 0.0)
-        k = sample_row<T>(v, b, rej, Kmax, up * W, d, lane);
+        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * W, d, lane);
       else
-        k = sample_row<T>(v, b, rej, Kmax, up * s_Z[rej], -1, lane);
+        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * s_Z[rej], -1, lane);
       if (lane == 0) v.next_token[b] = k;
     }
   }
 }
 
-// ---------------------------------------------------------------- residual (sampled drafts)
+// ---------------------------------------------------------------- residual draw
 template <typename T, bool VEC>
-__global__ __launch_bounds__(THREADS) void residual_kernel(const VerifyLaunch v) {
-  constexpr int VE = VecOf<T>::n;
-  const int chunk = blockIdx.x, b = blockIdx.y;
-  const WalkState st = v.ws[b];
-  if (st.rej < 0) return;
-  const int tid = threadIdx.x;
-  const int base = chunk * VCHUNK;
-  float xp[VCHUNK / THREADS], xq[VCHUNK / THREADS];
-  load_chunk<T, VEC>(row_ptr<T>(v, b, st.rej), v.V, base, tid, xp);
-  load_chunk<T, VEC>(row_ptr<T>(v, b, v.R + st.rej), v.V, base, tid, xq);
-  __shared__ float lds[kRounds<T> * THREADS];
-  float s[kRounds<T>];
-#pragma unroll
-  for (int k = 0; k < kRounds<T>; ++k) {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < VE; ++j) acc += residual_weight(xp[k * VE + j], xq[k * VE + j], st, v.c2);
-    s[k] = acc;
-  }
-  sub_sums<T>(s, lds, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
-}
-
-template <typename T>
 __global__ __launch_bounds__(64) void locate_kernel(const VerifyLaunch v) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const WalkState st = v.ws[b];
@@ -625,14 +655,23 @@ __global__ __launch_bounds__(64) void locate_kernel(const VerifyLaunch v) {
     auto subw = [&](int j) -> double { return (double)rs[j]; };
     double pre;
     const int js = find_sub(subw, v.NSUB, target, lane, pre);
-    auto elw = [&](int e) -> double {
-      return (double)residual_weight(to_f(rp[e]), to_f(rq[e]), st, v.c2);
-    };
-    const int e0 = js * VSUB;
-    k = find_elem(elw, e0, min(VSUB, v.V - e0), pre, target, lane);
+    const int e0 = js * VSUB, end = min(e0 + VSUB, v.V);
+    float xp[16], xq[16];
+    load16<T, VEC>(rp, e0 + lane * 16, end, xp);
+    load16<T, VEC>(rq, e0 + lane * 16, end, xq);
+    double w16[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      w16[t] = (e0 + lane * 16 + t < end) ? (double)residual_weight(xp[t], xq[t], st, v.c2) : 0.0;
+    k = find_in16(w16, e0, pre, target, lane);
   } else {
     // p <= q~ everywhere (only by rounding): draw from p itself
-    k = sample_row<T>(v, b, st.rej, st.kp, st.up * st.zp, -1, lane);
+    const size_t rowid = (size_t)b * v.RR + st.rej;
+    const float* cr = v.cref + rowid * v.SV;
+    __shared__ double s_fac[MAX_SV];
+    if (lane < v.SV) s_fac[lane] = exp2((double)cr[lane] - (double)st.kp);
+    __syncthreads();
+    k = sample_row<T, VEC>(v, b, st.rej, s_fac, st.up * st.zp, -1, lane);
   }
   if (lane == 0) v.next_token[b] = k;
 }
@@ -662,12 +701,12 @@ hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
   } else {
     stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
   }
-  walk_kernel<T><<<v.B, WALK_THREADS, 0, s>>>(v);
+  const dim3 g2(v.draft ? v.SV + 1 : 1, v.B);
+  if (vec) walk_residual_kernel<T, true><<<g2, THREADS, 0, s>>>(v);
+  else walk_residual_kernel<T, false><<<g2, THREADS, 0, s>>>(v);
   if (v.draft) {
-    const dim3 g3(v.SV, v.B);
-    if (vec) residual_kernel<T, true><<<g3, THREADS, 0, s>>>(v);
-    else residual_kernel<T, false><<<g3, THREADS, 0, s>>>(v);
-    locate_kernel<T><<<v.B, 64, 0, s>>>(v);
+    if (vec) locate_kernel<T, true><<<v.B, 64, 0, s>>>(v);
+    else locate_kernel<T, false><<<v.B, 64, 0, s>>>(v);
   }
   return hipGetLastError();
 }
