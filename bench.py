@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--verify-sets", type=int, default=3,
                     help="distinct seeded verification inputs rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--proj-row-major", action="store_true",
+                    help="run the projection on row-major weights instead of the packed layout")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager steps instead of HIP-graph replays of the same steps")
     ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
@@ -107,6 +109,8 @@ def main():
                           draft_ids=dt(v.draft_ids), uniforms=dt(v.uniforms)))
     pin = synth.proj_inputs(pcfg)
     P = dict(x=dt(pin.x), w=dt(pin.w), a=dt(pin.a), b=dt(pin.b), gate=dt(pin.gate))
+    # weights are packed once, outside the timed region, as a serving system would at load
+    packed = None if args.proj_row_major else isd.pack_proj_weights(P["w"], P["a"], P["b"])
     gen_s = time.time() - t0
 
     att_out = torch.empty_like(A["q"])
@@ -116,7 +120,10 @@ def main():
     def step(i, ev=None):
         if ev is not None:
             ev[0].record()
-        isd.gated_lora_proj(P["x"], P["w"], P["a"], P["b"], P["gate"], out=y)
+        if packed is None:
+            isd.gated_lora_proj(P["x"], P["w"], P["a"], P["b"], P["gate"], out=y)
+        else:
+            isd.gated_lora_proj_packed(P["x"], packed, P["gate"], out=y)
         if ev is not None:
             ev[1].record()
         isd.attention_step(A["q"], A["k_new"], A["v_new"], A["k_cache"], A["v_cache"],
@@ -224,6 +231,7 @@ def main():
             "kv_heads": scfg.Hkv, "head_dim": scfg.D, "page_size": 16,
             "context": f"U[{scfg.ctx[1]},{scfg.ctx[2]}]" if scfg.ctx[0] == "uniform" else scfg.ctx[1],
             "vocab": scfg.V, "proj": f"{pcfg.M}x{pcfg.K}->{pcfg.Nout} r{pcfg.r}",
+            "proj_weights": "row-major" if packed is None else "packed (MFMA fragment order)",
             "verify_input_sets": len(vsets),
         },
         "accepted_tokens_per_s": round(steps_per_s * scfg.B * tpf_hat, 1),

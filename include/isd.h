@@ -8,6 +8,7 @@
  *   isd_attention_step   strictly causal GQA attention of the block over a paged KV cache
  *   isd_verify           vocab-wide p/q verification, residual resampling, argmax proposals
  *   isd_gated_lora_proj  R-ISD projection: base weights on every row, LoRA delta on gated rows
+ *                        (also on weights packed once in MMA fragment order: *_packed)
  *
  * Conventions for every entry point
  *   - Tensor arguments are DEVICE pointers, dense and row-major in the shapes given, owned
@@ -148,6 +149,30 @@ size_t isd_gated_lora_workspace_bytes(int M, int K, int Nout, int r);
 isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, const void* b,
                                const uint8_t* gate, void* y, int M, int K, int Nout, int r,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- packed projection weights
+ * The same R-ISD projection on weights stored once in MFMA fragment order, so that the
+ * kernels read every weight byte with fully coalesced 1 KB loads and stage only the
+ * activations.  Results are bit-identical to isd_gated_lora_proj on the same x, w, a, b.
+ *
+ * Packed layout (bf16): S = [w; a] (Nout + r rows of K) as 1 KB fragments -- fragment
+ * (nb, kb), nb < (Nout + r)/16, kb < K/32, holds S[16 nb + l % 16][32 kb + 8 (l / 16) + e]
+ * at element ((nb (K/32) + kb) 64 + l) 8 + e for l < 64, e < 8 -- followed by b
+ * [Nout, r] unchanged.
+ *
+ * isd_proj_packed_bytes: size of the packed buffer (0 for unsupported shapes).
+ * isd_pack_proj_weights: writes the packed buffer from w [Nout,K], a [r,K], b [Nout,r]
+ *   (a, b unused when r == 0); asynchronous on `stream`.
+ * isd_gated_lora_proj_packed: as isd_gated_lora_proj with the packed buffer in place of
+ *   w, a, b; r is the rank the buffer was packed with (gate NULL => base only, any r).
+ * Requires: K % 64 == 0, Nout % 128 == 0, r in {0, 128, 256}, r > 0 when gated,
+ *   1 <= M <= 65536.  Workspace: isd_gated_lora_workspace_bytes(M, K, Nout, r). */
+size_t isd_proj_packed_bytes(int K, int Nout, int r);
+isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, void* packed, int K,
+                                 int Nout, int r, void* stream);
+isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const uint8_t* gate,
+                                      void* y, int M, int K, int Nout, int r, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -129,14 +129,6 @@ __device__ __forceinline__ void load_kv_page(const uint16_t* kt, const uint16_t*
     vf[n] = *reinterpret_cast<const u32x2*>(vt + n * 256 + lane * 4);
 }
 
-// Barrier that orders LDS only.  A plain workgroup barrier also waits for every
-// outstanding global load and store of the waves, which would drain the page pipeline.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Wave state (m, l, O) -> LDS, lane-contiguous so every access is conflict-free.
 template <int D, int QB>
 constexpr int state_floats() { return (2 * QB + QB * (D / 16) * 4) * 64; }

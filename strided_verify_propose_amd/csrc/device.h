@@ -100,4 +100,13 @@ __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 template <typename T>
 __device__ __forceinline__ T ldg(const T* p) { return *p; }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load and store of the waves, which drains any load pipeline that
+// runs across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace isd

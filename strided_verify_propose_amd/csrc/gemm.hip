@@ -15,24 +15,16 @@
 // reuse it from that XCD's L2.
 #include "device.h"
 #include "launch.h"
+#include "tiles.h"
 
 namespace isd {
 namespace {
 
 constexpr int BM = 64, BN = 128, BK = 64;
 constexpr int THREADS = 256;
-constexpr int XCDS = 8;
 constexpr int PROJ_RING = 4;  // register stages of the load pipeline
 constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte loads per thread per k step
 constexpr int B_LOADS = BN * BK / 8 / THREADS;
-
-// Barrier that orders LDS only.  A plain workgroup barrier also waits for every
-// outstanding global load, which would drain the load pipeline at every k step.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // One k step (64) of operand data in flight for one thread.  Loads are row-contiguous:
 // eight consecutive lanes read one row's 128 bytes.
@@ -152,15 +144,6 @@ __device__ void gemm_tile(Tiles (&lds)[2], const uint16_t* __restrict__ X, int l
   }
 }
 
-// Linear workgroup id -> (m tile, n tile): XCD x (= id % 8, the dispatch order) takes the
-// column blocks x, x + 8, ... with all their row tiles.
-__device__ __forceinline__ bool tile_of(int id, int mt, int nt, int& m, int& n) {
-  const int x = id % XCDS, k = id / XCDS;
-  n = x + XCDS * (k / mt);
-  m = k % mt;
-  return n < nt;
-}
-
 __global__ __launch_bounds__(THREADS) void base_kernel(const ProjLaunch p) {
   const int mt = (p.M + BM - 1) / BM, nt = (p.Nout + p.r) / BN;
   int tm, tn;
@@ -234,16 +217,18 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
     }
 }
 
-int grid_of(int M, int ncols) {
-  const int mt = (M + BM - 1) / BM, nt = ncols / BN;
-  return XCDS * ((nt + XCDS - 1) / XCDS) * mt;
-}
+int grid_of(int M, int ncols) { return tile_grid((M + BM - 1) / BM, ncols / BN); }
 
 }  // namespace
 
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s) {
   base_kernel<<<grid_of(p.M, p.Nout + p.r), THREADS, 0, s>>>(p);
   if (p.gate) lora_kernel<<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora(const ProjLaunch& p, hipStream_t s) {
+  lora_kernel<<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,210 @@
+// R-ISD gated projection on weights packed in MFMA fragment order (bf16 in/out):
+//   Y = X W + gate * bf16(X A) B,
+// the same product and the same rows-with-gate-0-are-base-only guarantee as the row-major
+// kernels (「首次超越 AR 模型」 "無損 R-ISD"; 「内省扩散语言模型」 "1. 引言";
+// 「I-DLM – introspektive Diffusion Language Models」 "Lossless R-ISD").
+//
+// Packed layout.  A weight matrix S of n rows (output columns) by k (the contraction)
+// is stored as 1 KB fragments: fragment (nb, kb), nb < n/16, kb < k/32, holds
+// S[16 nb + l % 16][32 kb + 8 (l / 16) + e] at element ((nb (k/32) + kb) 64 + l) 8 + e,
+// i.e. exactly the B operand of v_mfma_f32_16x16x32_bf16 for lane l.  The packed buffer
+// holds S = [W^T; A^T] (Nout + r rows of K) in that order, then B^T (Nout rows of r)
+// row-major: the second kernel (K = r, two k steps) is the row-major one.
+//
+// With the weights in that order every wave loads its B operands straight from memory
+// with 1 KB fully coalesced loads, and only the activation tile goes through LDS (stored
+// as fragments with the same conflict-free xor swizzle as the row-major kernels).
+// Tiles: 64 x 128 per workgroup, 4 waves of 64 x 32 (4 x 2 MFMA 16x16x32 blocks), K in
+// steps of 64 with three steps of loads in flight.
+#include "device.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace isd {
+namespace {
+
+constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int THREADS = 256;
+constexpr int RING = 4;                         // register stages of the load pipeline
+constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte activation loads per thread per k step
+constexpr int FRAG = 64 * 8;                    // elements in one packed 16 x 32 fragment
+
+// ---------------------------------------------------------------- packing
+// One thread per 16 bytes of the packed buffer: S = [W^T; A^T] in fragment order, then
+// B^T as it is (the second kernel reads it row-major).
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w,
+                                                   const uint16_t* __restrict__ a,
+                                                   const uint16_t* __restrict__ b,
+                                                   uint16_t* __restrict__ packed, int K, int Nout,
+                                                   int r) {
+  const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long gS = (long long)(Nout + r) * K / 8, gB = (long long)Nout * r / 8;
+  if (g >= gS + gB) return;
+  if (g >= gS) {
+    const long long h = g - gS;
+    *reinterpret_cast<u32x4*>(packed + (size_t)(Nout + r) * K + (size_t)h * 8) =
+        *reinterpret_cast<const u32x4*>(b + (size_t)h * 8);
+    return;
+  }
+  const int lane = (int)(g & 63);
+  const long long frag = g >> 6;
+  const int kb = (int)(frag % (K / 32)), nb = (int)(frag / (K / 32));
+  const int row = nb * 16 + (lane & 15), col = kb * 32 + 8 * (lane >> 4);
+  const uint16_t* src = row < Nout ? w + (size_t)row * K + col : a + (size_t)(row - Nout) * K + col;
+  *reinterpret_cast<u32x4*>(packed + (size_t)g * 8) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// ---------------------------------------------------------------- product
+struct Stage {
+  u32x4 a[A_LOADS];
+  u32x4 b[2][2];  // this wave's weight fragments [column block][k half]
+};
+
+// LDS activation tile: MFMA fragments [k half][16-row block][slot].  Row r, 16-byte k chunk
+// c (0..7) lives in fragment (c / 4, r / 16) at slot (c % 4) * 16 + ((r % 16) ^ c).
+struct ATile {
+  u32x4 f[2][BM / 16][64];
+};
+
+__device__ __forceinline__ int chunk_slot(int r, int c) { return (c & 3) * 16 + ((r & 15) ^ c); }
+
+__device__ __forceinline__ void issue(Stage& st, const uint16_t* const (&pa)[A_LOADS],
+                                      const uint16_t* const (&pb)[2], int s) {
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(pa[i] + s * BK);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      st.b[cb][kk] = *reinterpret_cast<const u32x4*>(pb[cb] + (size_t)(2 * s + kk) * FRAG);
+}
+
+__device__ __forceinline__ void put(ATile& t, const Stage& st, int tid) {
+  const int c = tid & 7;
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    t.f[c >> 2][r >> 4][chunk_slot(r, c)] = st.a[i];
+  }
+}
+
+struct Frags {
+  u32x4 a[2][BM / 16];  // [k half][row block]
+};
+
+__device__ __forceinline__ void fetch_frags(Frags& f, const ATile& t, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int slot = lane ^ (kk * 4 + (lane >> 4));
+#pragma unroll
+    for (int rb = 0; rb < BM / 16; ++rb) f.a[kk][rb] = t.f[kk][rb][slot];
+  }
+}
+
+__device__ __forceinline__ void mma(const Frags& f, const Stage& st, f32x4 (&acc)[BM / 16][2]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int rb = 0; rb < BM / 16; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma16x16x32(f.a[kk][rb], st.b[cb][kk], acc[rb][cb]);
+}
+
+// acc[rb][cb] = sum over k < K of X[16 rb + row][k] S[32 wave + 16 cb + col][k] for the
+// 64 x 128 tile at X and the packed fragments at Sp (the tile's first 16-column block).
+// X rows past `mrows` read row mrows - 1 (never stored).  At step s: loads for step
+// s + RING - 1 go out, step s + 2's activations go to LDS, step s + 1's activation
+// fragments come from LDS, and step s's MFMAs run.
+__device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int ldx, int mrows,
+                          const uint16_t* __restrict__ Sp, int K, int tid, int wave, int lane,
+                          f32x4 (&acc)[BM / 16][2]) {
+  static_assert(RING % 2 == 0 && RING >= 4, "fragment buffers alternate with the step parity");
+  const int KB = K / 32;
+  const uint16_t* pa[A_LOADS];
+  const uint16_t* pb[2];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i)
+    pa[i] = X + (size_t)min((tid >> 3) + 32 * i, mrows - 1) * ldx + (tid & 7) * 8;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) pb[cb] = Sp + ((size_t)(2 * wave + cb) * KB) * FRAG + lane * 8;
+#pragma unroll
+  for (int rb = 0; rb < BM / 16; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int S = K / BK;
+  Stage r[RING];
+  Frags f[2];
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) issue(r[u], pa, pb, min(u, S - 1));
+  put(lds[0], r[0], tid);
+  put(lds[1], r[1], tid);
+  lds_barrier();
+  fetch_frags(f[0], lds[0], lane);
+  // Steps past the end re-load and re-stage the last step (unconditional loads keep the
+  // compiler's wait counts exact); only the MFMAs are skipped.
+  for (int s0 = 0; s0 < S; s0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int s = s0 + u;
+      issue(r[(u + RING - 1) % RING], pa, pb, min(s + RING - 1, S - 1));
+      fetch_frags(f[(u + 1) & 1], lds[(s + 1) & 1], lane);
+      put(lds[s & 1], r[(u + 2) % RING], tid);
+      if (s < S) mma(f[u & 1], r[u], acc);
+      lds_barrier();
+    }
+  }
+}
+
+__global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p) {
+  const int mt = (p.M + BM - 1) / BM, nt = (p.Nout + p.r) / BN;
+  int tm, tn;
+  if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int mrows = min(BM, p.M - m0);
+  const bool lowrank = n0 >= p.Nout;  // this tile computes T = X A
+  const size_t blk = (size_t)(p.K / 32) * FRAG;  // elements per packed 16-column block
+  __shared__ ATile lds[2];
+  f32x4 acc[BM / 16][2];
+  gemm_tile(lds, p.X + (size_t)m0 * p.K, p.K, mrows, p.Sp + (size_t)(n0 / 16) * blk, p.K, tid, wave, lane, acc);
+#pragma unroll
+  for (int rb = 0; rb < BM / 16; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = rb * 16 + 4 * gq + e;
+      if (row >= mrows) continue;
+      const int gr = m0 + row;
+      const bool gated = p.gate != nullptr && p.gate[gr] != 0;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int col = n0 + wave * 32 + cb * 16 + l16;
+        const float v = acc[rb][cb][e];
+        if (lowrank)
+          p.T[(size_t)gr * p.r + (col - p.Nout)] = (uint16_t)f32_to_bf16_bits(v);
+        else if (gated)
+          p.Ybase[(size_t)gr * p.Nout + col] = v;
+        else
+          p.Y[(size_t)gr * p.Nout + col] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s) {
+  const int mt = (p.M + BM - 1) / BM;
+  base_kernel_packed<<<tile_grid(mt, (p.Nout + p.r) / BN), THREADS, 0, s>>>(p);
+  if (p.gate) return launch_lora(p, s);  // K = r: the row-major kernel on B^T as stored
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_proj(const uint16_t* w, const uint16_t* a, const uint16_t* b, uint16_t* packed,
+                            int K, int Nout, int r, hipStream_t s) {
+  const long long groups = (long long)(Nout + r) * K / 8 + (long long)Nout * r / 8;
+  pack_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(w, a, b, packed, K, Nout, r);
+  return hipGetLastError();
+}
+
+}  // namespace isd

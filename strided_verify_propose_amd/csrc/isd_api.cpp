@@ -253,4 +253,59 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
   return hip_status(isd::launch_proj(p, static_cast<hipStream_t>(stream)), "gated_lora_proj launch");
 }
 
+// ---------------------------------------------------------------- packed projection weights
+size_t isd_proj_packed_bytes(int K, int Nout, int r) {
+  if (K < 64 || K % 64 || Nout < 128 || Nout % 128 || (r != 0 && r != 128 && r != 256)) return 0;
+  return ((size_t)(Nout + r) * K + (size_t)Nout * r) * sizeof(uint16_t);
+}
+
+isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, void* packed, int K,
+                                 int Nout, int r, void* stream) {
+  if (!w || !packed) return fail(ISD_ERR_INVALID_ARG, "pack_proj_weights: null tensor pointer");
+  if (K < 64 || K % 64) return fail(ISD_ERR_UNSUPPORTED, "pack_proj_weights: K=%d (multiple of 64 required)", K);
+  if (Nout < 128 || Nout % 128)
+    return fail(ISD_ERR_UNSUPPORTED, "pack_proj_weights: Nout=%d (multiple of 128 required)", Nout);
+  if (r != 0 && r != 128 && r != 256)
+    return fail(ISD_ERR_UNSUPPORTED, "pack_proj_weights: r=%d (supported: 0, 128, 256)", r);
+  if (r > 0 && (!a || !b)) return fail(ISD_ERR_INVALID_ARG, "pack_proj_weights: r > 0 needs a and b");
+  return hip_status(isd::launch_pack_proj(static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(a),
+                                          static_cast<const uint16_t*>(b), static_cast<uint16_t*>(packed), K,
+                                          Nout, r, static_cast<hipStream_t>(stream)),
+                    "pack_proj_weights launch");
+}
+
+isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const uint8_t* gate, void* y, int M,
+                                      int K, int Nout, int r, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!x || !packed || !y) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj_packed: null tensor pointer");
+  if (M < 1 || M > 65536) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj_packed: M=%d out of [1, 65536]", M);
+  if (K < 64 || K % 64)
+    return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj_packed: K=%d (multiple of 64 required)", K);
+  if (Nout < 128 || Nout % 128)
+    return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj_packed: Nout=%d (multiple of 128 required)", Nout);
+  if (r != 0 && r != 128 && r != 256)
+    return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj_packed: r=%d (supported: 0, 128, 256)", r);
+  if (gate && r == 0) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj_packed: gate given with r=0");
+  const bool lora = gate != nullptr;
+  const ProjWs ws_ = proj_ws(M, K, Nout, lora ? r : 0);
+  if (lora && (!workspace || workspace_bytes < ws_.total))
+    return fail(ISD_ERR_WORKSPACE, "gated_lora_proj_packed: workspace %zu bytes, need %zu", workspace_bytes,
+                ws_.total);
+  char* ws = static_cast<char*>(workspace);
+  const uint16_t* pk = static_cast<const uint16_t*>(packed);
+  isd::ProjLaunch p{};
+  p.X = static_cast<const uint16_t*>(x);
+  p.Y = static_cast<uint16_t*>(y);
+  p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
+  p.Sp = pk;
+  if (lora) {
+    p.gate = gate;
+    p.r = r;
+    p.Bl = pk + (size_t)(Nout + r) * K;
+    p.Ybase = reinterpret_cast<float*>(ws + ws_.ybase);
+    p.T = reinterpret_cast<uint16_t*>(ws + ws_.T);
+  }
+  return hip_status(isd::launch_proj_packed(p, static_cast<hipStream_t>(stream)), "gated_lora_proj_packed launch");
+}
+
 }  // extern "C"

@@ -84,7 +84,13 @@ struct ProjLaunch {
   int M, K, Nout, r;            // r = 0 when ungated
   float* Ybase;                 // workspace [M, Nout] fp32 (rows with gate 1)
   uint16_t* T;                  // workspace [M, r] bf16
+  const uint16_t* Sp;           // packed path: [W^T; A^T] in fragment order
 };
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s);
+hipError_t launch_lora(const ProjLaunch& p, hipStream_t s);  // the second kernel alone
+hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s);
+// Pack [W^T; A^T] (Nout + r rows of K) into fragment order and copy B^T after it.
+hipError_t launch_pack_proj(const uint16_t* w, const uint16_t* a, const uint16_t* b, uint16_t* packed,
+                            int K, int Nout, int r, hipStream_t s);
 
 }  // namespace isd

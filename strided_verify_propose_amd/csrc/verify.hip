@@ -171,14 +171,6 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
   }
 }
 
-// Barrier that orders LDS only, so that loads already issued for the next chunk stay in
-// flight (a plain workgroup barrier waits for every outstanding load).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // The same statistics with 16-byte aligned rows, from a resident grid: workgroup w takes
 // the (row, chunk) units w, w + W, ... and keeps the next unit's loads in flight while it
 // reduces the current one.  Units are numbered (b RR + rr) SV + chunk.

@@ -24,7 +24,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
            "isd_verify_workspace_bytes", "isd_verify",
-           "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj")
+           "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
+           "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed")
 
 
 class IsdError(RuntimeError):
@@ -58,6 +59,12 @@ def lib() -> ctypes.CDLL:
     L.isd_gated_lora_workspace_bytes.argtypes = [i32] * 4
     L.isd_gated_lora_proj.restype = i32
     L.isd_gated_lora_proj.argtypes = [vp] * 6 + [i32] * 4 + [vp, sz, vp]
+    L.isd_proj_packed_bytes.restype = sz
+    L.isd_proj_packed_bytes.argtypes = [i32] * 3
+    L.isd_pack_proj_weights.restype = i32
+    L.isd_pack_proj_weights.argtypes = [vp] * 4 + [i32] * 3 + [vp]
+    L.isd_gated_lora_proj_packed.restype = i32
+    L.isd_gated_lora_proj_packed.argtypes = [vp] * 4 + [i32] * 4 + [vp, sz, vp]
     if L.isd_abi_version() != 1:
         raise RuntimeError("libisd.so ABI version mismatch")
     _lib = L
@@ -211,3 +218,55 @@ def gated_lora_proj(x, w, a=None, b=None, gate=None, out=None):
     _check(L.isd_gated_lora_proj(_ptr(x), _ptr(w), _ptr(a), _ptr(b), _ptr(gate), _ptr(out),
                                  M, K, Nout, r, _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+class PackedProj:
+    """Projection weights packed once in MFMA fragment order (isd_pack_proj_weights)."""
+
+    def __init__(self, data: torch.Tensor, K: int, Nout: int, r: int):
+        self.data, self.K, self.Nout, self.r = data, K, Nout, r
+
+
+def pack_proj_weights(w, a=None, b=None) -> PackedProj:
+    """Pack w [Nout,K] (= W^T), a [r,K] (= A^T), b [Nout,r] (= B^T) for
+    gated_lora_proj_packed (a, b None: base weights only)."""
+    Nout, K = w.shape
+    dev = w.device
+    bf = torch.bfloat16
+    _need(w, "w", bf, (Nout, K), dev)
+    r = 0
+    if a is not None or b is not None:
+        r = a.shape[0]
+        _need(a, "a", bf, (r, K), dev)
+        _need(b, "b", bf, (Nout, r), dev)
+    L = lib()
+    nbytes = L.isd_proj_packed_bytes(K, Nout, r)
+    if nbytes == 0:
+        raise IsdError(2, f"unsupported projection shape K={K} Nout={Nout} r={r}")
+    data = torch.empty(nbytes // 2, dtype=bf, device=dev)
+    _check(L.isd_pack_proj_weights(_ptr(w), _ptr(a), _ptr(b), _ptr(data), K, Nout, r, _stream(dev)))
+    return PackedProj(data, K, Nout, r)
+
+
+def gated_lora_proj_packed(x, packed: PackedProj, gate=None, out=None):
+    """gated_lora_proj on packed weights: y = x W + gate * bf16(x A) B (bf16)."""
+    M, K = x.shape
+    Nout, r = packed.Nout, packed.r
+    dev = x.device
+    bf = torch.bfloat16
+    if K != packed.K:
+        raise ValueError(f"x has K={K}, the weights were packed for K={packed.K}")
+    _need(x, "x", bf, device=dev)
+    if gate is not None:
+        _need(gate, "gate", torch.uint8, (M,), dev)
+    if out is None:
+        out = torch.empty((M, Nout), dtype=bf, device=dev)
+    _need(out, "out", bf, (M, Nout), dev)
+    L = lib()
+    rg = r if gate is not None else 0
+    nbytes = L.isd_gated_lora_workspace_bytes(M, K, Nout, rg)
+    ws = workspace("proj", nbytes, dev, (M, K, Nout, rg))
+    _check(L.isd_gated_lora_proj_packed(_ptr(x), _ptr(packed.data), _ptr(gate), _ptr(out), M, K, Nout, r,
+                                        _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+

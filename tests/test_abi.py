@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -119,6 +119,45 @@ def proj(L, **kw):
 ])
 def test_proj_validation(L, kw, status):
     assert proj(L, **kw) == status
+
+
+def proj_packed(L, **kw):
+    a = dict(M=448, K=4096, Nout=4096, r=128, gate=FAKE, packed=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.isd_gated_lora_proj_packed(FAKE, a["packed"], a["gate"], FAKE, a["M"], a["K"], a["Nout"],
+                                        a["r"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), INVALID),
+    (dict(packed=None), INVALID),
+    (dict(K=100), UNSUPPORTED),
+    (dict(Nout=200), UNSUPPORTED),
+    (dict(r=64), UNSUPPORTED),
+    (dict(r=0), INVALID),          # gated call on weights packed without a rank
+    (dict(wsb=1000), WORKSPACE),
+])
+def test_proj_packed_validation(L, kw, status):
+    assert proj_packed(L, **kw) == status
+
+
+@pytest.mark.parametrize("K,Nout,r,ok", [(4096, 4096, 128, True), (64, 128, 0, True), (64, 128, 256, True),
+                                        (100, 128, 0, False), (64, 100, 0, False), (64, 128, 64, False)])
+def test_proj_packed_bytes(L, K, Nout, r, ok):
+    n = L.isd_proj_packed_bytes(K, Nout, r)
+    assert n == (((Nout + r) * K + Nout * r) * 2 if ok else 0)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE, FAKE, 64, 128, 128), INVALID),
+    ((FAKE, FAKE, FAKE, None, 64, 128, 128), INVALID),
+    ((FAKE, None, FAKE, FAKE, 64, 128, 128), INVALID),   # rank without a
+    ((FAKE, FAKE, FAKE, FAKE, 96, 128, 128), UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 64, 192, 128), UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 64, 128, 96), UNSUPPORTED),
+])
+def test_pack_validation(L, args, status):
+    assert L.isd_pack_proj_weights(*args, None) == status
 
 
 def test_workspace_queries_grow_with_shape(L):

@@ -19,8 +19,15 @@ def run(M, K, Nout, r, seed, pattern=(0, 0, 0, 1, 1, 1, 1)):
     y = isd.gated_lora_proj(x, w, a, b, gate)
     y2 = isd.gated_lora_proj(x, w, a, b, gate)
     yb = isd.gated_lora_proj(x, w)
+    # the packed-weight path computes the same MFMA sequence: bit-identical results
+    pk = isd.pack_proj_weights(w, a, b)
+    yp = isd.gated_lora_proj_packed(x, pk, gate)
+    ybp = isd.gated_lora_proj_packed(x, pk)
+    ybp0 = isd.gated_lora_proj_packed(x, isd.pack_proj_weights(w))
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "not deterministic"
+    assert torch.equal(yp, y), "packed path differs from the row-major path"
+    assert torch.equal(ybp, yb) and torch.equal(ybp0, yb), "packed base-only path differs"
     g = p.gate.astype(bool)
     Y, Yb = to_np(y), to_np(yb)
     assert np.array_equal(Y[~g], Yb[~g]), "ungated rows differ from the base-only call"
@@ -44,3 +51,23 @@ def test_ragged_shapes(M, K, Nout, r):
 def test_all_gated_and_none_gated():
     run(64, 256, 128, 128, 3, pattern=(1,))
     run(64, 256, 128, 128, 4, pattern=(0,))
+
+
+def test_packed_layout():
+    """The packed buffer follows the documented layout: S = [w; a] in fragments, fragment
+    (nb, kb) holding S[16 nb + l % 16][32 kb + 8 (l / 16) + e] at ((nb (K/32) + kb) 64 + l) 8 + e,
+    then b as it is."""
+    rng = np.random.default_rng(5)
+    K, Nout, r = 128, 256, 128
+    w = rng.integers(0, 1 << 16, size=(Nout, K), dtype=np.uint16)
+    a = rng.integers(0, 1 << 16, size=(r, K), dtype=np.uint16)
+    b = rng.integers(0, 1 << 16, size=(Nout, r), dtype=np.uint16)
+    pk = isd.pack_proj_weights(to_dev(w), to_dev(a), to_dev(b))
+    got = to_np(pk.data)
+
+    def frag_order(S):
+        n, k = S.shape
+        return S.reshape(n // 16, 16, k // 32, 4, 8).transpose(0, 2, 3, 1, 4).ravel()
+
+    want = np.concatenate([frag_order(np.concatenate([w, a])), b.ravel()])
+    assert np.array_equal(got, want)
