@@ -7,19 +7,22 @@
 // rejection the next token comes from the normalised residual max(0, p - q~).
 //
 // Kernels (HBM-streaming reductions over the vocabulary; no MFMA):
-//   stats    grid (chunk, row, request): one 16384-entry chunk of one row per workgroup.
-//            Chunk max M of the raw logits, the lowest id holding it, the chunk reference
-//            K = M log2(e)/T rounded to fp32, and for every 1024-entry sub-chunk the sum
-//            of 2^(l log2(e)/T - K).  K is used exactly everywhere downstream, so every
-//            element weight has one rounding (the fma's) and no chunk carries a bias.
-//   walk     one workgroup (8 waves) per request: row max, argmax and normaliser from
-//            the chunk statistics in fp64; the acceptance walk; each inverse-CDF draw
-//            from an fp64 prefix over sub-chunk sums plus one re-read sub-chunk.
-//   residual grid (chunk, request), requests whose sampled draft was rejected only:
-//            per sub-chunk sums of max(0, p - q~) over the two rows involved.
+//   stats    per 16384-entry chunk of each row: the chunk max M of the raw logits, the
+//            lowest id holding it, the chunk reference K = M log2(e)/T rounded to fp32,
+//            and for every 1024-entry sub-chunk the sum of 2^(l log2(e)/T - K).  K is
+//            used exactly everywhere downstream, so every element weight has one rounding
+//            (the fma's) and no chunk carries a bias.  A resident grid walks the chunks
+//            with the next one's loads in flight (one workgroup per chunk when rows are not
+//            16-byte aligned).
+//   walk_residual  grid (chunks + 1, request) with sampled drafts, (1, request) with
+//            argmax drafts.  Every workgroup takes the request's walk from the chunk
+//            statistics in fp64 (row max, argmax, normaliser, acceptance); the last one
+//            writes the outputs and takes each inverse-CDF draw from an fp64 prefix over
+//            sub-chunk sums plus one re-read sub-chunk; the others sum max(0, p - q~) over
+//            their chunk's sub-chunks when the request's sampled draft was rejected.
 //   locate   one wave per such request: prefix over those sums, re-read one sub-chunk.
-// Argmax drafts (no draft rows) need no residual pass: the residual is p with the draft
-// removed, whose sub-chunk sums the stats pass already has.
+// Argmax drafts need no residual sums: the residual is p with the draft removed, whose
+// sub-chunk sums the stats pass already has.
 #include <limits.h>
 
 #include <atomic>
