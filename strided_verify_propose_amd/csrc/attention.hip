@@ -266,19 +266,26 @@ void attn_bf16_kernel(const AttnLaunch a) {
 
     // Issue first what needs no page id: Q^T fragments (B operand of S^T = K Q^T), the
     // page ids of this wave's first 64 full pages, the partial page's id, the block rows.
+    // These loads are unconditional, with indexes clamped into range and the lanes past
+    // the end zeroed after the loads: a load under a branch makes the compiler wait for
+    // every earlier load at the branch, one full memory round trip each.
     u32x4 qf[QB][D / 32];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int qr = (qb0 + j) * 16 + l16;
-      const int r = qr / G, hg = qr - r * G;
+      const int qc = min(qr, RG - 1);
+      const int r = qc / G, hg = qc - r * G;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        qf[j][c] = (qb0 + j < NQB && qr < RG)
-                       ? *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D +
-                                                         32 * c + 8 * g)
-                       : u32x4{0u, 0u, 0u, 0u};
+        qf[j][c] = *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 32 * c + 8 * g);
     }
-    int my_id = (c0 + 4 * lane < fend) ? page_id(pt, c0 + 4 * lane, a.num_pages) : 0;
+    int my_id = page_id(pt, min(c0 + 4 * lane, a.max_pages - 1), a.num_pages);
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+      if (qb0 + j >= NQB || (qb0 + j) * 16 + l16 >= RG)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[j][c] = u32x4{0u, 0u, 0u, 0u};
+    if (c0 + 4 * lane >= fend) my_id = 0;
 
     f32x4 o[QB][D / 16];
     float m[QB], l[QB];
@@ -292,21 +299,24 @@ void attn_bf16_kernel(const AttnLaunch a) {
     u32x4 kf[D / 32], kf2[D / 32];
     u32x2 vf[D / 16], vf2[D / 16];
 
-    if (do_block) {  // the block's own rows, from k_new / v_new
+    if (do_block) {  // the block's own rows, from k_new / v_new (rows past R zeroed)
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        kf2[c] = (l16 < R) ? *reinterpret_cast<const u32x4*>(kn_ + blk + l16 * rstride + 32 * c + 8 * g)
-                           : u32x4{0u, 0u, 0u, 0u};
+        kf2[c] = *reinterpret_cast<const u32x4*>(kn_ + blk + min(l16, R - 1) * rstride + 32 * c + 8 * g);
+      uint32_t h[D / 16][4];
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) h[n][t] = vn_[blk + min(4 * g + t, R - 1) * rstride + 16 * n + l16];
+      if (l16 >= R)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf2[c] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int n = 0; n < D / 16; ++n) {
-        uint32_t h[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int tok = 4 * g + t;
-          h[t] = (tok < R) ? vn_[blk + tok * rstride + 16 * n + l16] : 0u;
-        }
-        vf2[n][0] = h[0] | (h[1] << 16);
-        vf2[n][1] = h[2] | (h[3] << 16);
+        for (int t = 0; t < 4; ++t) h[n][t] = (4 * g + t < R) ? h[n][t] : 0u;
+        vf2[n][0] = h[n][0] | (h[n][1] << 16);
+        vf2[n][1] = h[n][2] | (h[n][3] << 16);
       }
     }
     if (do_partial) {
@@ -354,7 +364,10 @@ void attn_bf16_kernel(const AttnLaunch a) {
       } else {
         attend_tile<D, QB, 0>(kf, vf, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
       }
-      if (c0 + 256 < fend) my_id = (c0 + 256 + 4 * lane < fend) ? page_id(pt, c0 + 256 + 4 * lane, a.num_pages) : 0;
+      if (c0 + 256 < fend) {
+        my_id = page_id(pt, min(c0 + 256 + 4 * lane, a.max_pages - 1), a.num_pages);
+        if (c0 + 256 + 4 * lane >= fend) my_id = 0;
+      }
     }
 
     // Merge the group's four wave states: all four go to LDS, then wave k of the group
