@@ -36,6 +36,10 @@ namespace {
 constexpr int THREADS = 256;
 constexpr int MAX_RR = 22;    // 2N-1 + N-1 rows for N <= 8
 constexpr int MAX_SV = 64;    // vocab <= 2^20
+constexpr int RPB = 3;        // rows per wave per batch of loads in the walk
+constexpr int CSL = 3;        // sub-chunk sums per lane per row held in registers there
+constexpr int STASH = 4096;   // sub-chunk sums the walk keeps in LDS
+constexpr int RSPLIT = 1;     // residual workgroups per stats chunk (2 and 4 measured slower)
 
 template <typename T> struct VecOf;
 template <> struct VecOf<uint16_t> { static constexpr int n = 8; };
@@ -70,12 +74,12 @@ __device__ __forceinline__ const T* row_ptr(const VerifyLaunch& v, int b, int rr
 
 // Load one chunk of a row into registers: thread t, round k holds entries
 // base + k*THREADS*VE + t*VE + [0, VE).  Entries past V read as -inf.
-template <typename T, bool VEC>
+template <typename T, bool VEC, int ROUNDS = kRounds<T>>
 __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int V, int base, int tid,
-                                           float (&x)[VCHUNK / THREADS]) {
+                                           float (&x)[ROUNDS * VecOf<T>::n]) {
   constexpr int VE = VecOf<T>::n;
 #pragma unroll
-  for (int k = 0; k < kRounds<T>; ++k) {
+  for (int k = 0; k < ROUNDS; ++k) {
     const int e0 = base + k * THREADS * VE + tid * VE;
     if (VEC && e0 + VE <= V) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(row + e0);
@@ -99,17 +103,19 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int V, int
 
 // Per-thread round sums -> sub-chunk sums, in a fixed order: the round sums go to LDS,
 // then 16 lanes per sub-chunk add their consecutive share and reduce in their 16-lane group.
-template <typename T>
-__device__ __forceinline__ void sub_sums(const float (&s)[kRounds<T>], float* lds, float* out,
+template <typename T, int ROUNDS = kRounds<T>>
+__device__ __forceinline__ void sub_sums(const float (&s)[ROUNDS], float* lds, float* out,
                                          int chunk, int nsub, int tid) {
   constexpr int VE = VecOf<T>::n;
   constexpr int TPS = VSUB / VE;              // threads covering one sub-chunk in a round
   constexpr int SPR = THREADS / TPS;          // sub-chunks per round
   constexpr int PER = TPS / 16;               // round sums per lane
+  constexpr int SUBS = ROUNDS * SPR;          // sub-chunks of this chunk
 #pragma unroll
-  for (int k = 0; k < kRounds<T>; ++k) lds[k * THREADS + tid] = s[k];
+  for (int k = 0; k < ROUNDS; ++k) lds[k * THREADS + tid] = s[k];
   __syncthreads();
   const int j = tid >> 4, p = tid & 15;       // sub-chunk of this chunk, lane in its group
+  if (j >= SUBS) return;
   const float* src = lds + (j / SPR) * THREADS + (j % SPR) * TPS + p * PER;
   float v = 0.f;
 #pragma unroll
@@ -118,7 +124,7 @@ __device__ __forceinline__ void sub_sums(const float (&s)[kRounds<T>], float* ld
   v += __shfl_xor(v, 4);
   v += __shfl_xor(v, 2);
   v += __shfl_xor(v, 1);
-  const int sub = chunk * VCHUNK_SUBS + j;
+  const int sub = chunk * SUBS + j;
   if (p == 0 && sub < nsub) out[sub] = v;
 }
 
@@ -418,11 +424,11 @@ __device__ int find_in16(const double (&w16)[16], int e0, double pre, double tar
 // removed.  fac[c] = 2^(K_c - Kmax) for chunk c of this row.
 template <typename T, bool VEC>
 __device__ int sample_row(const VerifyLaunch& v, int b, int rr, const double* fac, double target,
-                          int excl, int lane) {
+                          int excl, int lane, const float* cs_stash = nullptr) {
   const T* __restrict__ row = row_ptr<T>(v, b, rr);
   const size_t rowid = (size_t)b * v.RR + rr;
   const float* __restrict__ cr = v.cref + rowid * v.SV;
-  const float* __restrict__ cs = v.csub + rowid * v.NSUB;
+  const float* cs = cs_stash ? cs_stash : v.csub + rowid * v.NSUB;
   double wex = 0.0;
   int exsub = -1;
   if (excl >= 0) {
@@ -453,10 +459,11 @@ __device__ int sample_row(const VerifyLaunch& v, int b, int rr, const double* fa
 }
 
 // ---------------------------------------------------------------- walk + residual
-// Grid (chunks + 1, requests) with sampled drafts, (1, requests) with argmax drafts.  Every
-// workgroup takes its request's acceptance walk from the row statistics (a few KB, the same
-// arithmetic in each); the last workgroup of a request writes the walk's outputs and takes
-// the inverse-CDF draws, and with sampled drafts the others each sum their chunk of the
+// Grid (residual chunks + 1, requests) with sampled drafts, (1, requests) with argmax
+// drafts; a residual chunk is 1/RSPLIT of a stats chunk.  Every workgroup takes its
+// request's acceptance walk from the row statistics (a few KB, the same arithmetic in
+// each); the last workgroup of a request writes the walk's outputs and takes the
+// inverse-CDF draws, and with sampled drafts the others each sum their chunk of the
 // residual max(0, p - q~) of a rejecting request.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaunch v) {
@@ -471,12 +478,14 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
   __shared__ int s_arg[MAX_RR];
   __shared__ double s_Z[MAX_RR];
   __shared__ double s_fac[MAX_RR][MAX_SV];
+  __shared__ float s_cs[STASH];  // sub-chunk sums of every row, when RR * NSUB fits
   __shared__ float s_lp[8], s_lq[8];
   __shared__ int s_rej;
   __shared__ double s_a, s_u;
   __shared__ WalkState s_st;
 
-  // logits at the draft ids, gathered in parallel
+  // logits at the draft ids, gathered in parallel (two dependent round trips, which the
+  // row loads below overlap)
   if (tid < N - 1) {
     const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + tid], 0), v.V - 1);
     s_lp[tid] = to_f(lg[((size_t)b * R + tid) * v.V + d]);
@@ -488,54 +497,87 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
 
   // A. per row (one wave each; the proposal rows only in the lead workgroup): raw max
   //    and its lowest id, reference Kmax, chunk factors 2^(K_c - Kmax) and
-  //    Z = sum_k 2^(l_k c2 - Kmax) over the sub-chunk sums (fp64)
-  for (int rr = wave; rr < RR; rr += WAVES) {
-    if (!lead && rr >= N - 1 && rr < R) continue;
-    const size_t rowid = (size_t)b * RR + rr;
-    const float* cm = v.cmax + rowid * SV;
-    const float* cr = v.cref + rowid * SV;
-    const int32_t* ci = v.cidx + rowid * SV;
-    const float* cs = v.csub + rowid * NSUB;
-    const float mv = (lane < SV) ? cm[lane] : -__builtin_inff();
-    const float kv = (lane < SV) ? cr[lane] : -__builtin_inff();
-    const int iv = (lane < SV) ? ci[lane] : INT_MAX;
-    const float M = wave_max(mv);
-    const float Kmax = wave_max(kv);
-    const int arg = wave_min_i(mv == M ? iv : INT_MAX);
-    const double fl = (lane < SV) ? exp2((double)kv - (double)Kmax) : 0.0;
-    if (lane < SV) s_fac[rr][lane] = fl;
-    double z = 0.0;
-    for (int j0 = 0; j0 < NSUB; j0 += 64) {
-      const int j = j0 + lane;
-      const double f = __shfl(fl, min(j, NSUB - 1) / VCHUNK_SUBS);
-      if (j < NSUB) z += (double)cs[j] * f;
+  //    Z = sum_k 2^(l_k c2 - Kmax) over the sub-chunk sums (fp64).  A wave issues the
+  //    loads of all its rows of a batch before it uses any, so a batch costs one round
+  //    trip; the sub-chunk sums are kept in LDS for the draws when they fit.
+  const bool stash = RR * NSUB <= STASH;
+  for (int r0 = wave; r0 < RR; r0 += WAVES * RPB) {
+    float mv[RPB], kv[RPB], cv[RPB][CSL];
+    int iv[RPB];
+#pragma unroll
+    for (int q = 0; q < RPB; ++q) {
+      const size_t rowid = (size_t)b * RR + min(r0 + q * WAVES, RR - 1);
+      const int c = min(lane, SV - 1);
+      mv[q] = v.cmax[rowid * SV + c];
+      kv[q] = v.cref[rowid * SV + c];
+      iv[q] = v.cidx[rowid * SV + c];
+#pragma unroll
+      for (int t = 0; t < CSL; ++t) cv[q][t] = v.csub[rowid * NSUB + min(t * 64 + lane, NSUB - 1)];
     }
-    z = wave_sum_d(z);
-    if (lane == 0) {
-      s_K[rr] = Kmax;
-      s_arg[rr] = arg;
-      s_Z[rr] = z;
+#pragma unroll
+    for (int q = 0; q < RPB; ++q) {
+      const int rr = r0 + q * WAVES;
+      if (rr >= RR || (!lead && rr >= N - 1 && rr < R)) continue;
+      const float* cs = v.csub + ((size_t)b * RR + rr) * NSUB;
+      const float m = (lane < SV) ? mv[q] : -__builtin_inff();
+      const float k = (lane < SV) ? kv[q] : -__builtin_inff();
+      const float M = wave_max(m);
+      const float Kmax = wave_max(k);
+      const int arg = wave_min_i(m == M && lane < SV ? iv[q] : INT_MAX);
+      const double fl = (lane < SV) ? exp2((double)k - (double)Kmax) : 0.0;
+      if (lane < SV) s_fac[rr][lane] = fl;
+      double z = 0.0;
+#pragma unroll
+      for (int t = 0; t < CSL; ++t) {
+        const int j = t * 64 + lane;
+        const double f = __shfl(fl, min(j, NSUB - 1) / VCHUNK_SUBS);
+        if (j < NSUB) {
+          z += (double)cv[q][t] * f;
+          if (stash) s_cs[rr * NSUB + j] = cv[q][t];
+        }
+      }
+      for (int j0 = CSL * 64; j0 < NSUB; j0 += 64) {
+        const int j = j0 + lane;
+        const double f = __shfl(fl, min(j, NSUB - 1) / VCHUNK_SUBS);
+        if (j < NSUB) {
+          const float cj = cs[j];
+          z += (double)cj * f;
+          if (stash) s_cs[rr * NSUB + j] = cj;
+        }
+      }
+      z = wave_sum_d(z);
+      if (lane == 0) {
+        s_K[rr] = Kmax;
+        s_arg[rr] = arg;
+        s_Z[rr] = z;
+        if (lead && v.row_lse)
+          v.row_lse[(size_t)b * (R + N - 1) + rr] = (float)(((double)Kmax + log2(z)) * 0.6931471805599453);
+      }
     }
   }
   __syncthreads();
 
-  // B. the acceptance walk (one thread; everything it needs is in LDS)
-  if (tid == 0) {
+  // rows without statistics (no draft rows with argmax drafts) report 0
+  if (lead && v.row_lse && tid >= RR && tid < R + N - 1) v.row_lse[(size_t)b * (R + N - 1) + tid] = 0.f;
+
+  // B. p(d_i), q~(d_i) and the acceptance ratios, one thread per draft; then the walk
+  //    (one thread; everything it needs is in LDS)
+  __shared__ double s_ratio[8];
+  if (tid < N - 1) {
+    const int i = tid;
     const double c2 = v.c2;
-    const double ln2 = 0.6931471805599453;
-    if (lead && v.row_lse) {
-      for (int rr = 0; rr < R + N - 1; ++rr)
-        v.row_lse[(size_t)b * (R + N - 1) + rr] =
-            (rr < RR) ? (float)(((double)s_K[rr] + log2(s_Z[rr])) * ln2) : 0.f;
-    }
+    const double P = exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
+    const double Q = dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
+    if (lead && v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
+    if (lead && v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
+    s_ratio[i] = (P >= Q) ? 1.0 : P / Q;
+  }
+  __syncthreads();
+  if (tid == 0) {
     int rej = -1;
     double ra = 1.0, ru = 0.0;
     for (int i = 0; i < N - 1; ++i) {
-      const double P = exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
-      const double Q = dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
-      if (lead && v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
-      if (lead && v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
-      const double a = (P >= Q) ? 1.0 : P / Q;
+      const double a = s_ratio[i];
       uint8_t acc = 0;
       if (rej < 0) {
         const double u = (double)v.u[(size_t)b * R + i];
@@ -583,20 +625,21 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     const WalkState st = s_st;
     if (st.rej < 0) return;
     constexpr int VE = VecOf<T>::n;
-    const int base = chunk * VCHUNK;
-    float xp[VCHUNK / THREADS], xq[VCHUNK / THREADS];
-    load_chunk<T, VEC>(row_ptr<T>(v, b, st.rej), v.V, base, tid, xp);
-    load_chunk<T, VEC>(row_ptr<T>(v, b, v.R + st.rej), v.V, base, tid, xq);
-    __shared__ float lds[kRounds<T> * THREADS];
-    float sr[kRounds<T>];
+    constexpr int RR_ = kRounds<T> / RSPLIT;  // rounds of a residual chunk
+    const int base = chunk * (VCHUNK / RSPLIT);
+    float xp[RR_ * VE], xq[RR_ * VE];
+    load_chunk<T, VEC, RR_>(row_ptr<T>(v, b, st.rej), v.V, base, tid, xp);
+    load_chunk<T, VEC, RR_>(row_ptr<T>(v, b, v.R + st.rej), v.V, base, tid, xq);
+    __shared__ float lds[RR_ * THREADS];
+    float sr[RR_];
 #pragma unroll
-    for (int k = 0; k < kRounds<T>; ++k) {
+    for (int k = 0; k < RR_; ++k) {
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < VE; ++j) acc += residual_weight(xp[k * VE + j], xq[k * VE + j], st, v.c2);
       sr[k] = acc;
     }
-    sub_sums<T>(sr, lds, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
+    sub_sums<T, RR_>(sr, lds, v.rsub + (size_t)b * v.NSUB, chunk, v.NSUB, tid);
     return;
   }
 
@@ -608,7 +651,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     if (jb < N) {
       const int rr = N - 1 + jb;
       const double u = (double)v.u[(size_t)b * R + rr];
-      k = sample_row<T, VEC>(v, b, rr, s_fac[rr], u * s_Z[rr], -1, lane);
+      k = sample_row<T, VEC>(v, b, rr, s_fac[rr], u * s_Z[rr], -1, lane, stash ? s_cs + rr * NSUB : nullptr);
       if (lane == 0) {
         v.sampled_ids[(size_t)b * N + jb] = k;
         v.argmax_ids[(size_t)b * N + jb] = s_arg[rr];
@@ -623,10 +666,11 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       const double wd = (double)rel_weight(to_f(row[d]), cr[c], v.c2) * s_fac[rej][c];
       const double W = s_Z[rej] - wd;
       const double up = (s_u - s_a) / (1.0 - s_a);
+      const float* cst = stash ? s_cs + rej * NSUB : nullptr;
       if (W > 0.0)
-        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * W, d, lane);
+        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * W, d, lane, cst);
       else
-        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * s_Z[rej], -1, lane);
+        k = sample_row<T, VEC>(v, b, rej, s_fac[rej], up * s_Z[rej], -1, lane, cst);
       if (lane == 0) v.next_token[b] = k;
     }
   }
@@ -636,18 +680,36 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
 template <typename T, bool VEC>
 __global__ __launch_bounds__(64) void locate_kernel(const VerifyLaunch v) {
   const int b = blockIdx.x, lane = threadIdx.x;
+  // the walk state and the residual sums in one round trip; the sums go to LDS
   const WalkState st = v.ws[b];
-  if (st.rej < 0) return;
   const float* rs = v.rsub + (size_t)b * v.NSUB;
+  __shared__ float s_rs[MAX_SV * VCHUNK_SUBS];
+  float rv[CSL];
+#pragma unroll
+  for (int t = 0; t < CSL; ++t) rv[t] = rs[min(t * 64 + lane, v.NSUB - 1)];
+  if (st.rej < 0) return;
   double W = 0.0;
-  for (int j = lane; j < v.NSUB; j += 64) W += (double)rs[j];
+#pragma unroll
+  for (int t = 0; t < CSL; ++t) {
+    const int j = t * 64 + lane;
+    if (j < v.NSUB) {
+      W += (double)rv[t];
+      s_rs[j] = rv[t];
+    }
+  }
+  for (int j = CSL * 64 + lane; j < v.NSUB; j += 64) {
+    const float r = rs[j];
+    W += (double)r;
+    s_rs[j] = r;
+  }
   W = wave_sum_d(W);
+  __syncthreads();
   int k;
   if (W > 0.0) {
     const T* rp = row_ptr<T>(v, b, st.rej);
     const T* rq = row_ptr<T>(v, b, v.R + st.rej);
     const double target = st.up * W;
-    auto subw = [&](int j) -> double { return (double)rs[j]; };
+    auto subw = [&](int j) -> double { return (double)s_rs[j]; };
     double pre;
     const int js = find_sub(subw, v.NSUB, target, lane, pre);
     const int e0 = js * VSUB, end = min(e0 + VSUB, v.V);
@@ -696,7 +758,7 @@ hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
   } else {
     stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
   }
-  const dim3 g2(v.draft ? v.SV + 1 : 1, v.B);
+  const dim3 g2(v.draft ? (v.NSUB + VCHUNK_SUBS / RSPLIT - 1) / (VCHUNK_SUBS / RSPLIT) + 1 : 1, v.B);
   if (vec) walk_residual_kernel<T, true><<<g2, THREADS, 0, s>>>(v);
   else walk_residual_kernel<T, false><<<g2, THREADS, 0, s>>>(v);
   if (v.draft) {
