@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="concurrency sweep instead of the single benchmark line: one JSON line "
+                         "per (N, C) point, contexts fixed at 2048, inputs generated on the device")
+    ap.add_argument("--sweep-c", default="1,4,16,64,128,256")
+    ap.add_argument("--sweep-n", default="2,3,4")
     return ap.parse_args()
 
 
@@ -77,6 +82,9 @@ def main():
               f"(requests shard by data parallelism with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
     import torch
 
     from strided_verify_propose_amd import isd, synth
@@ -255,6 +263,136 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(scfg, att, ver0, pin)
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------- concurrency sweep
+SWEEP_SIGMA = 0.25  # proposal noise sd giving acceptance near 0.9 with anchor sd 3
+
+
+def sweep(args):
+    """Steps/s and tokens/s of the whole step against the number of concurrent requests C
+    (one request = one 2N-1 row block), for each stride N: where the block stops being
+    memory-bound.  Qwen3-8B attention shapes with every context at 2048 tokens, the
+    151936-entry vocabulary, the 4096 x 4096 r128 projection on C (2N-1) rows with the
+    [MASK] rows gated.  Inputs are drawn on the device (torch generator seeded per point),
+    the verification inputs in four rotated sets; each point times 50 replays of a HIP
+    graph per set after an eager pass that times each call with events."""
+    import torch
+
+    from strided_verify_propose_amd import isd
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Hq, Hkv, D, V, L, PAGE = 32, 8, 128, 151936, 2048, 16
+    K, Nout, r = 4096, 4096, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1300)
+    w = (torch.randn((Nout, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    a = (torch.randn((r, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    b = (torch.randn((Nout, r), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    packed = isd.pack_proj_weights(w, a, b)
+    del w, a, b
+    Cs = [int(c) for c in args.sweep_c.split(",")]
+    Ns = [int(n) for n in args.sweep_n.split(",")]
+    for pi, (N, C) in enumerate([(n, c) for n in Ns for c in Cs]):
+        gen.manual_seed(1400 + pi)
+        R = 2 * N - 1
+        bf = torch.bfloat16
+
+        def randn(*shape, sd=1.0):
+            return torch.randn(shape, generator=gen, device=dev) * sd
+
+        npg = (L + R + PAGE - 1) // PAGE
+        perm = torch.randperm(C * npg, generator=gen, device=dev).to(torch.int32)
+        A = dict(q=randn(C, R, Hq, D).to(bf), k_new=randn(C, R, Hkv, D).to(bf), v_new=randn(C, R, Hkv, D).to(bf),
+                 k_cache=randn(C * npg, Hkv, D // 8, PAGE, 8).to(bf),
+                 v_cache=randn(C * npg, Hkv, D // 16, 4, PAGE, 4).to(bf),
+                 page_table=perm.view(C, npg).contiguous(),
+                 ctx_lens=torch.full((C,), L, dtype=torch.int32, device=dev))
+        vsets = []
+        for _ in range(4):
+            anchor = randn(C, R, V, sd=3.0)
+            prop = anchor + randn(C, R, V, sd=SWEEP_SIGMA)
+            logits = torch.cat([anchor[:, :N - 1], prop[:, N - 1:]], dim=1).to(bf).contiguous()
+            draft = prop[:, :N - 1].to(bf).contiguous()
+            del anchor, prop
+            u01 = torch.rand(draft.shape, generator=gen, device=dev, dtype=torch.float64)
+            ids = torch.argmax(draft.double() - torch.log(-torch.log(u01)), dim=-1).to(torch.int32).contiguous()
+            del u01
+            u = (torch.randint(0, 1 << 24, (C, R), generator=gen, device=dev) / float(1 << 24)).to(torch.float32)
+            vsets.append((logits, draft, ids, u))
+        M = C * R
+        x = randn(M, K).to(bf)
+        gate = torch.tensor(([0] * (N - 1) + [1] * N) * C, dtype=torch.uint8, device=dev)
+        y = torch.empty((M, Nout), dtype=bf, device=dev)
+        att_out = torch.empty_like(A["q"])
+        vouts = [None] * len(vsets)
+
+        def step(i, ev=None):
+            if ev is not None:
+                ev[0].record()
+            isd.gated_lora_proj_packed(x, packed, gate, out=y)
+            if ev is not None:
+                ev[1].record()
+            isd.attention_step(A["q"], A["k_new"], A["v_new"], A["k_cache"], A["v_cache"],
+                               A["page_table"], A["ctx_lens"], L, out=att_out)
+            if ev is not None:
+                ev[2].record()
+            k = i % len(vsets)
+            vouts[k] = isd.verify(*vsets[k], with_diagnostics=False, out=vouts[k])
+            if ev is not None:
+                ev[3].record()
+
+        for i in range(8):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(20)]
+        for i, e in enumerate(evs):
+            step(i, e)
+        torch.cuda.synchronize()
+        us = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j in range(3)]
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for k in range(len(vsets)):
+                step(k)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs = []
+        for k in range(len(vsets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        steps = 50
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        n_acc = np.concatenate([vo["n_accept"].cpu().numpy() for vo in vouts])
+        rej = n_acc < N - 1
+        p_hat = float(np.sum(n_acc) / max(1, np.sum(n_acc + rej))) if N > 1 else 1.0
+        tpf = tpf_closed_form(N, p_hat) if N > 1 else 1.0
+        sps = steps / el
+        a_bytes = attention_bytes(np.full(C, L), R, Hq, Hkv, D)
+        v_bytes = verify_bytes(C, N, V, int(rej.sum() / len(vsets)))
+        p_flops = 2 * M * K * Nout + 2 * (C * N) * K * r + 2 * (C * N) * r * Nout
+        print(json.dumps({
+            "sweep": "concurrency", "stride_N": N, "C": C, "context": L, "query_rows": R,
+            "ms_per_step": round(1e3 * el / steps, 4), "steps_per_s": round(sps, 1),
+            "tokens_per_s": round(sps * C * tpf, 1), "p_hat": round(p_hat, 4),
+            "tpf_closed_form_at_p_hat": round(tpf, 4),
+            "us": {"gated_lora_proj": round(us[0], 2), "attention": round(us[1], 2), "verify": round(us[2], 2)},
+            "attention_hbm_frac": round(a_bytes / (us[1] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "verify_hbm_frac": round(v_bytes / (us[2] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "proj_mfma_frac": round(p_flops / (us[0] * 1e-6) / 2.5e15, 4),
+            "timing": "hip graph replay of whole steps; per-call times from an eager pass",
+            "data": "synthetic"}), flush=True)
+        del A, vsets, vouts, graphs, x, y, att_out
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):
