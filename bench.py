@@ -47,6 +47,8 @@ def parse():
                     help="concurrency sweep instead of the single benchmark line: one JSON line "
                          "per (N, C) point, contexts fixed at 2048, inputs generated on the device")
     ap.add_argument("--sweep-c", default="1,4,16,64,128,256")
+    ap.add_argument("--closed-loop", action="store_true",
+                    help="closed decoding loop on the device instead of the single benchmark line")
     ap.add_argument("--sweep-n", default="2,3,4")
     return ap.parse_args()
 
@@ -84,6 +86,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.closed_loop:
+        closed_loop(args)
         return
     import torch
 
@@ -393,6 +398,75 @@ def sweep(args):
             "data": "synthetic"}), flush=True)
         del A, vsets, vouts, graphs, x, y, att_out
         torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- closed loop
+def closed_loop(args):
+    """Closed-loop decoding of the benchmark workload (64 requests, N = 4, contexts from
+    U[512, 4096], the projection on the block's rows): each step's outputs feed the next
+    step on the device (contexts, drafts, draft rows), one HIP graph per step replayed
+    `--steps` times.  Reports the tokens kept per forward against the closed form at the
+    measured acceptance rate, the hot path's time per step (events around the library's
+    calls in an eager pass), the synthetic model's time apart, and graph against eager
+    launch.  One JSON line."""
+    import torch
+
+    from strided_verify_propose_amd.loop import ClosedLoop, LoopConfig
+    steps = max(args.steps, 20)
+    cfg = LoopConfig(B=64, N=4, steps=steps + 40 + args.warmup)
+    lp = ClosedLoop(cfg)
+    for _ in range(args.warmup):
+        lp.step()
+    torch.cuda.synchronize()
+    # eager pass: events around the model, the hot path's calls and the bookkeeping
+    n_ev = 20
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_ev)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        lp.model()
+        lp.hot_path(e[1:6])
+        lp.keep_draft_rows()
+        e[6].record()
+    torch.cuda.synchronize()
+    eager_ms = 1e3 * (time.perf_counter() - t0) / n_ev
+    seg = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs])) * 1e3
+    model_us = seg(0, 1) + seg(5, 6)
+    proj_us, att_us, ver_us, commit_us = seg(1, 2), seg(2, 3), seg(3, 4), seg(4, 5)
+    hot_us = seg(1, 5)
+    # reset the totals, then time graph replays
+    for t in (lp.kept, lp.accepted, lp.evaluated, lp.hot_steps):
+        t.zero_()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lp.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    if hasattr(g, "register_generator_state"):
+        g.register_generator_state(lp.gen)
+    with torch.cuda.graph(g):
+        lp.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = lp.stats(steps + 2)     # the capture-stream step and the captured step ran too
+    tpf = st["tpf_meas"]
+    print(json.dumps({
+        "closed_loop": "isd_qwen3_8b_b64_n4", "steps": steps, "data": "synthetic",
+        "graph_ms_per_step": round(1e3 * el / steps, 4), "eager_ms_per_step": round(eager_ms, 4),
+        "hot_path_us": {"gated_lora_proj": round(proj_us, 2), "attention": round(att_us, 2),
+                        "verify": round(ver_us, 2), "commit": round(commit_us, 2), "total": round(hot_us, 2)},
+        "synthetic_model_and_tallies_us": round(model_us, 2),
+        "tpf_meas": round(tpf, 4), "tpf_se": round(st["tpf_se"], 4), "p_hat": round(st["p_hat"], 4),
+        "tpf_closed_form_at_p_hat": round(st["tpf_closed_form_at_p_hat"], 4),
+        "kept_tokens_per_s_hot_path": round(cfg.B * tpf / (hot_us * 1e-6), 1),
+        "kept_tokens_per_s_with_model": round(cfg.B * tpf * steps / el, 1),
+    }), flush=True)
 
 
 def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):

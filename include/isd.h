@@ -111,7 +111,9 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
  *   draft_logits  [B, N-1, V]    row i is q~_i, the distribution d_i was drawn from (the
  *                 previous step's proposal row); NULL => argmax drafts: q~_i is one-hot on
  *                 d_i, so a_i = p_i(d_i) and the residual is p_i with d_i removed
- *   draft_ids     [B, N-1] int32 in [0, V)
+ *   draft_ids     [B, N-1] int32 in [0, V); draft_ids[b][0] < 0 marks a cold request (no
+ *                 valid drafts: no walk, n_accept 0, P = Q = 0, and next_token is the
+ *                 inverse-CDF draw of row 0 -- the anchor of the next position -- at u[b][0])
  *   uniforms      [B, R] float in [0, 1): u[b][i] for draft i's test (reused as
  *                 (u - a)/(1 - a) for the residual draw), u[b][N-1+j] for proposal row j
  * Walk: a_i = 1 if P >= Q else P/Q with P = p_i(d_i), Q = q~_i(d_i); accept iff u < a_i;
@@ -134,6 +136,25 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
                       int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
                       float* p_draft, float* q_draft, float* row_lse, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- commit
+ * What one step keeps, per request -- the two-state chain of tokens per forward
+ * (「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor Explorer"; the step
+ * that cannot verify emits one exact token and fresh proposals, "Inference & ISD").
+ * The step's block held the last committed token c (position ctx_len), then the drafts.
+ *   n_accept, next_token [B], sampled_ids [B, N]: isd_verify's outputs for the step
+ *   draft_ids [B, N-1] in/out: in, the step's drafts (draft_ids[b][0] < 0 marks a cold
+ *             request, as in isd_verify); out, the next step's drafts -- sampled_ids[b][1..N-1]
+ *             when the step was cold or accepted all N-1 drafts, else -1 (the next step is
+ *             cold: those proposals followed a rejected token).  May be NULL when N == 1.
+ *   ctx_lens [B] in/out: grows by the number of tokens kept, n_accept + 1 (1 when cold)
+ *   tokens [B, N] out, may be NULL: the kept tokens (accepted drafts, then next_token),
+ *             padded with -1
+ *   counts [B] out, may be NULL: the number kept
+ * All device pointers; asynchronous on the stream.  Requires 1 <= N <= 8. */
+isd_status isd_commit(const int32_t* n_accept, const int32_t* next_token, const int32_t* sampled_ids,
+                      int32_t* draft_ids, int32_t* ctx_lens, int32_t* tokens, int32_t* counts, int B, int N,
+                      void* stream);
 
 /* ---------------------------------------------------------------- R-ISD projection
  * Gated residual adaptation of one linear layer: the LoRA delta is applied only on gated

@@ -19,4 +19,5 @@ from . import attention, chain, proj, stored, verify  # noqa: F401
 from .attention import attention_step  # noqa: F401
 from .chain import efficiency, renewal_estimate, simulate_chain, tpf_closed_form  # noqa: F401
 from .proj import gated_lora_proj  # noqa: F401
+from .verify import commit as commit_step  # noqa: F401
 from .verify import verify as verify_step  # noqa: F401

@@ -30,6 +30,14 @@ Steps, per request (all float64):
   6. sampled_ids[j] = inverse-CDF draw of proposal row j at u_{N-1+j}
 Inverse CDF: the smallest k with (w_0 + ... + w_k) > u * sum(w), ids ascending.
 
+Cold requests.  After a rejection the new proposals were made after a token that was
+then rejected, so the next step has no valid drafts (「I-DLM – introspektive Diffusion
+Language Models」 "Inference & ISD": the step that cannot verify emits one exact token and
+fresh proposals).  A request whose draft_ids[b][0] is negative is such a cold request:
+no walk (n_accept 0, nothing accepted, P = Q = 0), and the next token is the inverse-CDF
+draw of row 0 -- the anchor of the next position -- at u_0.  Its proposal rows and
+samples are as for any request.
+
 Every draw is also checked against the boundaries it was compared with: a draw whose
 uniform lies within `eps` of one (in u-space) is flagged, since a correct
 implementation in another precision may fall on either side of it.
@@ -123,6 +131,13 @@ def verify(logits, draft_logits, draft_ids, uniforms, N, temperature=1.0, eps=1e
             res["sampled_ids"][b, j] = k
             res["sample_flag"][b, j] = abs(u - lo) < eps or abs(u - hi) < eps
 
+        if N > 1 and int(d_all[b, 0]) < 0:             # cold: one exact token from row 0
+            u = u_all[b, 0]
+            k, lo, hi = inverse_cdf(probs[0], u)
+            res["next_token"][b] = k
+            res["residual_flag"][b] = abs(u - lo) < eps or abs(u - hi) < eps
+            continue
+
         rejected = None
         for i in range(N - 1):                          # the acceptance walk
             d = int(d_all[b, i])
@@ -165,6 +180,39 @@ def verify(logits, draft_logits, draft_ids, uniforms, N, temperature=1.0, eps=1e
 
 
 def emitted_tokens(res, draft_ids, b):
-    """Tokens a request commits this step: accepted drafts, then the next token."""
+    """Tokens a request commits this step: accepted drafts, then the next token (a cold
+    request accepts none)."""
     n = int(res["n_accept"][b])
     return [int(t) for t in draft_ids[b, :n]] + [int(res["next_token"][b])]
+
+
+def commit(n_accept, next_token, sampled_ids, draft_ids, ctx_lens, N):
+    """State of every request after one step (the two-state chain of tokens per
+    forward, 「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor
+    Explorer", with the slots of one strided block).
+
+    The block held [c, d_1 .. d_{N-1}, MASK ..] (hot) or [c, MASK ..] (cold), c being the
+    last committed token at position ctx_len.  The step keeps c and the n accepted
+    drafts, so ctx_len grows by n + 1 and next_token becomes the new c.  The next step is
+    hot -- drafts sampled_ids[1 .. N-1], drawn from the [MASK] rows -- when this step
+    was cold or accepted every draft; otherwise those proposals followed a rejected
+    token and the next step is cold (draft ids -1).
+
+    Returns (ctx_lens', draft_ids', emitted tokens [B, N] padded with -1, count [B])."""
+    n_accept = np.asarray(n_accept)
+    draft_ids = np.asarray(draft_ids)
+    B = len(n_accept)
+    ctx = np.asarray(ctx_lens).astype(np.int64).copy()
+    nxt = np.full((B, max(N - 1, 0)), -1, np.int32)
+    out = np.full((B, N), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    for b in range(B):
+        cold = N > 1 and int(draft_ids[b, 0]) < 0
+        n = 0 if cold else int(n_accept[b])
+        toks = [int(t) for t in draft_ids[b, :n]] + [int(next_token[b])]
+        out[b, :len(toks)] = toks
+        cnt[b] = len(toks)
+        ctx[b] += len(toks)
+        if N > 1 and (cold or n == N - 1):
+            nxt[b] = np.asarray(sampled_ids)[b, 1:N]
+    return ctx.astype(np.int32), nxt, out, cnt

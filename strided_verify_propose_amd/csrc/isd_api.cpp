@@ -259,6 +259,20 @@ size_t isd_proj_packed_bytes(int K, int Nout, int r) {
   return ((size_t)(Nout + r) * K + (size_t)Nout * r) * sizeof(uint16_t);
 }
 
+isd_status isd_commit(const int32_t* n_accept, const int32_t* next_token, const int32_t* sampled_ids,
+                      int32_t* draft_ids, int32_t* ctx_lens, int32_t* tokens, int32_t* counts, int B, int N,
+                      void* stream) {
+  if (B < 1 || B > (1 << 24)) return fail(ISD_ERR_INVALID_ARG, "commit: B=%d out of [1, 2^24]", B);
+  if (N < 1 || N > 8) return fail(ISD_ERR_UNSUPPORTED, "commit: N=%d (supported: 1..8)", N);
+  if (!n_accept || !next_token || !sampled_ids || !ctx_lens || (N > 1 && !draft_ids))
+    return fail(ISD_ERR_INVALID_ARG, "commit: null pointer");
+  isd::CommitLaunch c{};
+  c.n_accept = n_accept; c.next_token = next_token; c.sampled_ids = sampled_ids;
+  c.draft_ids = draft_ids; c.ctx_lens = ctx_lens; c.tokens = tokens; c.counts = counts;
+  c.B = B; c.N = N;
+  return hip_status(isd::launch_commit(c, static_cast<hipStream_t>(stream)), "commit launch");
+}
+
 isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, void* packed, int K,
                                  int Nout, int r, void* stream) {
   if (!w || !packed) return fail(ISD_ERR_INVALID_ARG, "pack_proj_weights: null tensor pointer");

@@ -73,6 +73,19 @@ struct VerifyLaunch {
 };
 hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);
 
+// ---------------------------------------------------------------- commit
+struct CommitLaunch {
+  const int32_t* n_accept;      // [B]
+  const int32_t* next_token;    // [B]
+  const int32_t* sampled_ids;   // [B][N]
+  int32_t* draft_ids;           // [B][N-1] in: this step's drafts; out: the next step's
+  int32_t* ctx_lens;            // [B] in/out
+  int32_t* tokens;              // [B][N] committed tokens, -1 padded; may be null
+  int32_t* counts;              // [B] number committed; may be null
+  int B, N;
+};
+hipError_t launch_commit(const CommitLaunch& c, hipStream_t s);
+
 // ---------------------------------------------------------------- gated projection
 struct ProjLaunch {
   const uint16_t* X;            // [M, K]

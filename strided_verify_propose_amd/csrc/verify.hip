@@ -484,6 +484,9 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
   __shared__ double s_a, s_u;
   __shared__ WalkState s_st;
 
+  // a cold request (draft_ids[b][0] < 0) has no valid drafts
+  const bool cold = N > 1 && v.draft_ids[(size_t)b * (N - 1)] < 0;
+
   // logits at the draft ids, gathered in parallel (two dependent round trips, which the
   // row loads below overlap)
   if (tid < N - 1) {
@@ -562,12 +565,13 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
 
   // B. p(d_i), q~(d_i) and the acceptance ratios, one thread per draft; then the walk
   //    (one thread; everything it needs is in LDS)
+  //    A cold request (draft_ids[b][0] < 0: no valid drafts) takes no walk.
   __shared__ double s_ratio[8];
   if (tid < N - 1) {
     const int i = tid;
     const double c2 = v.c2;
-    const double P = exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
-    const double Q = dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
+    const double P = cold ? 0.0 : exp2((double)s_lp[i] * c2 - (double)s_K[i]) / s_Z[i];
+    const double Q = cold ? 0.0 : dl ? exp2((double)s_lq[i] * c2 - (double)s_K[R + i]) / s_Z[R + i] : 1.0;
     if (lead && v.p_draft) v.p_draft[(size_t)b * (N - 1) + i] = (float)P;
     if (lead && v.q_draft) v.q_draft[(size_t)b * (N - 1) + i] = (float)Q;
     s_ratio[i] = (P >= Q) ? 1.0 : P / Q;
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
   if (tid == 0) {
     int rej = -1;
     double ra = 1.0, ru = 0.0;
-    for (int i = 0; i < N - 1; ++i) {
+    for (int i = 0; i < N - 1 && !cold; ++i) {
       const double a = s_ratio[i];
       uint8_t acc = 0;
       if (rej < 0) {
@@ -591,7 +595,9 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       }
       if (lead) v.accept[(size_t)b * (N - 1) + i] = acc;
     }
-    if (lead) v.n_accept[b] = (rej < 0) ? N - 1 : rej;
+    if (lead && cold)
+      for (int i = 0; i < N - 1; ++i) v.accept[(size_t)b * (N - 1) + i] = 0;
+    if (lead) v.n_accept[b] = cold ? 0 : (rej < 0) ? N - 1 : rej;
     s_rej = rej;
     s_a = ra;
     s_u = ru;
@@ -645,7 +651,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
 
   // D. inverse-CDF draws, one wave each: N proposal rows, plus the argmax-draft residual
   const bool argmax_residual = (rej >= 0) && (dl == nullptr);
-  const int jobs = N + (argmax_residual ? 1 : 0);
+  const int jobs = N + ((argmax_residual || cold) ? 1 : 0);
   for (int jb = wave; jb < jobs; jb += WAVES) {
     int k;
     if (jb < N) {
@@ -655,8 +661,13 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       if (lane == 0) {
         v.sampled_ids[(size_t)b * N + jb] = k;
         v.argmax_ids[(size_t)b * N + jb] = s_arg[rr];
-        if (jb == 0 && rej < 0) v.next_token[b] = k;
+        if (jb == 0 && rej < 0 && !cold) v.next_token[b] = k;
       }
+    } else if (cold) {
+      // no valid drafts: the exact token of the next position from row 0 at u_0
+      k = sample_row<T, VEC>(v, b, 0, s_fac[0], (double)v.u[(size_t)b * R] * s_Z[0], -1, lane,
+                             stash ? s_cs : nullptr);
+      if (lane == 0) v.next_token[b] = k;
     } else {
       // residual of a one-hot q~: p_rej with the draft removed, drawn at (u - a)/(1 - a)
       const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + rej], 0), v.V - 1);

@@ -25,7 +25,8 @@ EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
            "isd_verify_workspace_bytes", "isd_verify",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
-           "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed")
+           "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed",
+           "isd_commit")
 
 
 class IsdError(RuntimeError):
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.isd_pack_proj_weights.argtypes = [vp] * 4 + [i32] * 3 + [vp]
     L.isd_gated_lora_proj_packed.restype = i32
     L.isd_gated_lora_proj_packed.argtypes = [vp] * 4 + [i32] * 4 + [vp, sz, vp]
+    L.isd_commit.restype = ctypes.c_int
+    L.isd_commit.argtypes = [vp] * 7 + [i32] * 2 + [vp]
     if L.isd_abi_version() != 1:
         raise RuntimeError("libisd.so ABI version mismatch")
     _lib = L
@@ -191,6 +194,27 @@ def verify(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
                         _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
                         _ptr(out.get("row_lse")), _ptr(w), w.numel(), _stream(dev)))
     return out
+
+
+def commit(n_accept, next_token, sampled_ids, draft_ids, ctx_lens, tokens=None, counts=None):
+    """Advance every request by one step (isd_commit): ctx_lens grows by the tokens kept,
+    draft_ids becomes the next step's drafts (-1 rows: cold).  n_accept, next_token [B],
+    sampled_ids [B,N]: isd_verify's outputs; draft_ids [B,N-1], ctx_lens [B] int32 are
+    updated in place; tokens [B,N] and counts [B] (int32, optional) receive the kept
+    tokens and their number."""
+    B, N = sampled_ids.shape
+    dev = sampled_ids.device
+    for name, t, shape in (("n_accept", n_accept, (B,)), ("next_token", next_token, (B,)),
+                           ("draft_ids", draft_ids, (B, N - 1)), ("ctx_lens", ctx_lens, (B,))):
+        _need(t, name, torch.int32, shape, dev)
+    _need(sampled_ids, "sampled_ids", torch.int32, (B, N), dev)
+    if tokens is not None:
+        _need(tokens, "tokens", torch.int32, (B, N), dev)
+    if counts is not None:
+        _need(counts, "counts", torch.int32, (B,), dev)
+    L = lib()
+    _check(L.isd_commit(_ptr(n_accept), _ptr(next_token), _ptr(sampled_ids), _ptr(draft_ids),
+                        _ptr(ctx_lens), _ptr(tokens), _ptr(counts), B, N, _stream(dev)))
 
 
 # ----------------------------------------------------------------------------- projection

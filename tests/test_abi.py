@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -166,3 +166,16 @@ def test_workspace_queries_grow_with_shape(L):
     assert 0 < small < big
     assert L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 128) > \
         L.isd_gated_lora_workspace_bytes(448, 4096, 4096, 0) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, 4), INVALID),        # B < 1
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 9), UNSUPPORTED),        # N > 8
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 0), UNSUPPORTED),        # N < 1
+    ((None, FAKE, FAKE, FAKE, FAKE, None, None, 4, 4), INVALID),      # null n_accept
+    ((FAKE, FAKE, FAKE, None, FAKE, None, None, 4, 4), INVALID),      # null draft ids, N > 1
+    ((FAKE, FAKE, FAKE, FAKE, None, None, None, 4, 4), INVALID),      # null ctx_lens
+])
+def test_commit_validation(L, args, status):
+    """Checked on the host before any launch (no GPU needed)."""
+    assert L.isd_commit(*args, None) == status

@@ -112,3 +112,48 @@ def test_emitted_token_law_through_kernel(argmax):
     stat = chisquare(np.bincount(first, minlength=V), p * n)
     print(f"  chi-square {stat.statistic:.2f} (7 dof), p-value {stat.pvalue:.3g}", flush=True)
     assert stat.statistic < 24.32       # 7 dof, alpha = 1e-3
+
+
+@pytest.mark.parametrize("argmax", [False, True])
+def test_verify_cold_requests(argmax):
+    """Every third request is cold (draft_ids[b][0] = -1): no walk, the next token drawn
+    from row 0 at u_0; the others are ordinary.  Parity with the oracle on the whole batch."""
+    c = cfg("cold_argmax" if argmax else "cold", "bf16", 24, 4, 151936, 51, argmax=argmax)
+    v = synth.verify_inputs(c)
+    d = v.draft_ids.copy()
+    d[::3] = -1
+    print(f"verify cold mix argmax={argmax}: {int((d[:, 0] < 0).sum())} cold of {c.B}", flush=True)
+    ref = oracle.verify_step(v.logits, v.draft_logits, d, v.uniforms, c.N)
+    out = isd.verify(to_dev(v.logits), None if v.draft_logits is None else to_dev(v.draft_logits),
+                     to_dev(d), to_dev(v.uniforms))
+    torch.cuda.synchronize()
+    compared, excluded = verify_parity(out, ref, c.N)
+    assert np.all(to_np(out["n_accept"])[::3] == 0) and np.all(to_np(out["accept"])[::3] == 0)
+    assert np.all(to_np(out["p_draft"])[::3] == 0)
+    print(f"  compared {compared}, excluded {excluded}", flush=True)
+
+
+def test_commit_matches_oracle():
+    """isd_commit against the oracle's commit on a random mix of hot (all accepted or
+    not) and cold requests, N in {1, 2, 4, 8}."""
+    rng = np.random.default_rng(61)
+    for N in (1, 2, 4, 8):
+        B = 300
+        n_acc = rng.integers(0, N, size=B).astype(np.int32)
+        nxt = rng.integers(0, 1000, size=B).astype(np.int32)
+        smp = rng.integers(0, 1000, size=(B, N)).astype(np.int32)
+        drafts = rng.integers(0, 1000, size=(B, N - 1)).astype(np.int32)
+        if N > 1:
+            drafts[rng.random(B) < 0.3] = -1
+        ctx = rng.integers(0, 5000, size=B).astype(np.int32)
+        ctx_r, nxt_d, toks_r, cnt_r = oracle.commit_step(n_acc, nxt, smp, drafts, ctx, N)
+        D = to_dev(drafts)
+        C = to_dev(ctx)
+        toks = torch.empty((B, N), dtype=torch.int32, device="cuda")
+        cnt = torch.empty(B, dtype=torch.int32, device="cuda")
+        isd.commit(to_dev(n_acc), to_dev(nxt), to_dev(smp), D, C, toks, cnt)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(C), ctx_r), N
+        assert np.array_equal(to_np(D), nxt_d), N
+        assert np.array_equal(to_np(toks), toks_r), N
+        assert np.array_equal(to_np(cnt), cnt_r), N
