@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--sweep-c", default="1,4,16,64,128,256")
     ap.add_argument("--closed-loop", action="store_true",
                     help="closed decoding loop on the device instead of the single benchmark line")
+    ap.add_argument("--layer", action="store_true",
+                    help="R-ISD decoder layer (Qwen3-8B shapes): gated against base-only time")
     ap.add_argument("--sweep-n", default="2,3,4")
     return ap.parse_args()
 
@@ -89,6 +91,9 @@ def main():
         return
     if args.closed_loop:
         closed_loop(args)
+        return
+    if args.layer:
+        layer_alpha(args)
         return
     import torch
 
@@ -467,6 +472,61 @@ def closed_loop(args):
         "kept_tokens_per_s_hot_path": round(cfg.B * tpf / (hot_us * 1e-6), 1),
         "kept_tokens_per_s_with_model": round(cfg.B * tpf * steps / el, 1),
     }), flush=True)
+
+
+# ---------------------------------------------------------------- R-ISD layer
+def layer_alpha(args):
+    """The R-ISD overhead alpha at the scale of a decoder layer: one Qwen3-8B-shaped layer
+    (seven linears with rank-128 deltas on the gated rows, attention over contexts from
+    U[512, 4096]) on 64 requests x 7 rows, gated against base-only, each as a HIP graph
+    replayed `--steps` times; the linears are timed one by one with events."""
+    import torch
+
+    from strided_verify_propose_amd import isd
+    from strided_verify_propose_amd.layer import LayerConfig, RIsdLayer
+    lay = RIsdLayer(LayerConfig())
+    res = {}
+    for gated in (False, True):
+        for _ in range(3):
+            lay.forward(gated)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            lay.forward(gated)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay.forward(gated)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        res[gated] = 1e6 * (time.perf_counter() - t0) / args.steps
+        del g
+    per = {}
+    gate = lay.gate
+    for name, pk in lay.packed.items():
+        x = torch.randn((lay.M, pk.K), device="cuda").to(torch.bfloat16)
+        us = []
+        for gt in (None, gate):
+            for _ in range(3):
+                isd.gated_lora_proj_packed(x, pk, gt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                isd.gated_lora_proj_packed(x, pk, gt)
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) / 20 * 1e3)
+        per[name] = {"K": pk.K, "Nout": pk.Nout, "base_us": round(us[0], 2), "gated_us": round(us[1], 2)}
+    print(json.dumps({"layer": "r_isd_qwen3_8b_b64_n4", "rows": lay.M, "rank": lay.cfg.r, "data": "synthetic",
+                      "base_only_us": round(res[False], 2), "gated_us": round(res[True], 2),
+                      "alpha": round(res[True] / res[False], 4), "linears": per,
+                      "timing": "hip graph replay of the layer; linears with events (warm weights)"}), flush=True)
 
 
 def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):
