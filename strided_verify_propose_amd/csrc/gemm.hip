@@ -190,13 +190,21 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
   const int l16 = lane & 15, gq = lane >> 4;
   const int m0 = tm * BM, n0 = tn * BN;
   const int mrows = min(BM, p.M - m0);
-  // skip tiles without gated rows
-  __shared__ int s_any;
-  if (tid == 0) s_any = 0;
-  __syncthreads();
-  if (tid < mrows && p.gate[m0 + tid]) s_any = 1;
-  __syncthreads();
-  if (!s_any) return;
+  // The gate flags and the base product of this lane's elements are loaded first (rows
+  // past the tile's end read its last row and are never written), so their round trip
+  // overlaps the delta's loads instead of following its product.
+  bool gated[2][4];
+  float yb[2][4][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = wm * 32 + i * 16 + 4 * gq + e;
+      const int gr = m0 + min(row, mrows - 1);
+      gated[i][e] = p.gate[gr] != 0 && row < mrows;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yb[i][j][e] = p.Ybase[(size_t)gr * p.Nout + n0 + wn * 64 + j * 16 + l16];
+    }
   __shared__ Tiles lds[2];
   f32x4 acc[2][4];
   gemm_tile<PROJ_RING>(lds, p.T + (size_t)m0 * p.r, p.r, mrows, p.Bl + (size_t)n0 * p.r, p.r, p.r, tid, wm, wn,
@@ -205,14 +213,12 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = wm * 32 + i * 16 + 4 * gq + e;
-      if (row >= mrows) continue;
-      const int gr = m0 + row;
-      if (!p.gate[gr]) continue;
+      if (!gated[i][e]) continue;
+      const int gr = m0 + wm * 32 + i * 16 + 4 * gq + e;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const size_t o = (size_t)gr * p.Nout + n0 + wn * 64 + j * 16 + l16;
-        p.Y[o] = (uint16_t)f32_to_bf16_bits(p.Ybase[o] + acc[i][j][e]);
+        p.Y[o] = (uint16_t)f32_to_bf16_bits(yb[i][j][e] + acc[i][j][e]);
       }
     }
 }
