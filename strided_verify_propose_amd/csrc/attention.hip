@@ -236,7 +236,6 @@ void attn_bf16_kernel(const AttnLaunch a) {
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
 
   int first = 1;  // no piece processed yet (selects the partial-result slot)
-  int tag0 = -1, tag1 = -1;  // items whose partials went to slots 2w and 2w + 1
   for (int cur = lo; cur < hi;) {
     // the item (b, kvh) holding cost position `cur`, and this workgroup's piece of it
     const int b = find_request(pre, a.B, cur);
@@ -379,7 +378,6 @@ void attn_bf16_kernel(const AttnLaunch a) {
     lds_barrier();
     const bool whole = (unit0 == 0 && unit1 == u);
     const size_t slot = (size_t)w * 2 + (first ? 0 : 1);
-    if (!whole) (first ? tag0 : tag1) = b * Hkv + kvh;
     float* po = a.part_o + slot * RG * D;
     float* pml = a.part_ml + slot * RG * 2;
     uint16_t* out = static_cast<uint16_t*>(a.out);
@@ -428,78 +426,92 @@ void attn_bf16_kernel(const AttnLaunch a) {
     lds_barrier();  // every wave has read the stashed states before they are overwritten
     first = 0;
   }
-  if (threadIdx.x == 0) {
-    a.part_tag[2 * w] = tag0;
-    a.part_tag[2 * w + 1] = tag1;
-  }
 }
 
 // After every read of the cache: write the block's K/V rows into their page slots and
-// merge the pieces of items that crossed workgroup boundaries.  The pieces of an item sit
-// in consecutive workgroups, so their slots are found by one scan of the slot tags and
-// merged in workgroup order.
+// merge the pieces of items that crossed workgroup boundaries.  Which workgroups hold
+// pieces of an item, and in which of their two slots, follows from the same cost list
+// the main kernel split (rebuilt here from the context lengths): workgroup w holds a
+// piece iff its share meets the item's real units, in slot 2w + 1 if its share began
+// before the item (it already wrote a piece of an earlier item), else in slot 2w.  The
+// pieces are merged in workgroup order.
 constexpr int COMBINE_THREADS = 256;
+static_assert(COMBINE_THREADS == 4 * 64, "the combine's few-piece path maps thread -> (piece, row) as 4 x 64");
+constexpr int APPEND_V = 8;  // V elements of the block per thread (R * D <= 15 * 128 < 8 * 256)
 
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const AttnLaunch a, int W) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int item = b * a.Hkv + kvh;
-  const int R = a.R, G = a.G, Hq = a.Hq, RG = R * G;
-  __shared__ int s_lo, s_hi;
-  if (threadIdx.x == 0) {
-    s_lo = 2 * W;
-    s_hi = -1;
-  }
-  lds_barrier();
-  for (int t = threadIdx.x; t < 2 * W; t += COMBINE_THREADS)
-    if (a.part_tag[t] == item) {
-      atomicMin(&s_lo, t);
-      atomicMax(&s_hi, t);
-    }
-
-  // append: K in 16-byte units of 8 dims, V element by element
+  const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
+  const int tid = threadIdx.x;
+  // the block's K (16-byte units of 8 dims) and V (elements) go out with the context
+  // lengths; the page ids of their slots follow once the length is known
+  const int L = clamp_len(a, b);
+  const size_t rstride = (size_t)Hkv * D;
+  const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
+  const uint16_t* kn_ = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn_ = static_cast<const uint16_t*>(a.v_new);
+  const int nk = R * (D / 8), nv = R * D;
+  u32x4 kval = u32x4{0u, 0u, 0u, 0u};
+  uint16_t vval[APPEND_V];
   {
-    const int L = clamp_len(a, b), Hkv = a.Hkv;
+    const int e = min(tid, nk - 1), t = e / (D / 8), d8 = e - t * (D / 8);
+    kval = *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
+#pragma unroll
+    for (int q = 0; q < APPEND_V; ++q) {
+      const int ev = min(tid + q * COMBINE_THREADS, nv - 1), tv = ev / D, d = ev - tv * D;
+      vval[q] = vn_[blk + tv * rstride + d];
+    }
+  }
+  __shared__ int pre[MAX_B + 1];
+  build_prefix(a, pre);
+  const int T = pre[a.B];
+
+  // append (after every read of the cache: the main kernel has finished)
+  {
     const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
     const size_t tile = (size_t)PAGE * D;
-    const size_t rstride = (size_t)Hkv * D;
-    const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
     uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
     uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    const uint16_t* kn_ = static_cast<const uint16_t*>(a.k_new);
-    const uint16_t* vn_ = static_cast<const uint16_t*>(a.v_new);
-    for (int e = threadIdx.x; e < R * (D / 8); e += COMBINE_THREADS) {
-      const int t = e / (D / 8), d8 = e - t * (D / 8);
-      const int j = L + t;
+    if (tid < nk) {
+      const int t = tid / (D / 8), d8 = tid - t * (D / 8), j = L + t;
       const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-      *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) =
-          *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
+      *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) = kval;
     }
-    for (int e = threadIdx.x; e < R * D; e += COMBINE_THREADS) {
-      const int t = e / D, d = e - t * D;
-      const int j = L + t, slot = j % PAGE;
+#pragma unroll
+    for (int q = 0; q < APPEND_V; ++q) {
+      const int ev = tid + q * COMBINE_THREADS;
+      if (ev >= nv) break;
+      const int tv = ev / D, d = ev - tv * D, j = L + tv, slot = j % PAGE;
       const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] = vn_[blk + t * rstride + d];
+      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] = vval[q];
     }
   }
-  lds_barrier();  // s_lo, s_hi complete (the append stores need not be)
-  if (s_hi < 0) return;  // one workgroup held the whole item and wrote its output
-  // Piece k sits in workgroup w0 + k: the first piece in slot s_lo, the others in the
-  // first slot of their workgroup (their share starts inside this item); workgroups with
-  // empty shares hold none.  Wave 0 lists the slots in order.
+
+  // this item's cost interval [c0, iend): start-up share, then its u real units
+  const int u = units_of(L);
+  const int c0 = pre[b] + kvh * (u + ITEM_COST), istart = c0 + ITEM_COST, iend = istart + u;
+  // workgroups whose shares meet [istart, iend): from the one holding istart to the one
+  // holding iend - 1 (largest w with range_lo(w) <= x)
+  auto holder = [&](int x) -> int {
+    int w = (int)min<long long>(W - 1, ((long long)(x + 1) * W + T - 1) / T - 1);
+    while (w > 0 && range_lo(w, T, W) > x) --w;
+    while (w + 1 < W && range_lo(w + 1, T, W) <= x) ++w;
+    return w;
+  };
+  const int w0 = holder(istart), w1 = holder(iend - 1);
+  if (w0 == w1) return;  // one workgroup held the whole item and wrote its output
   __shared__ int s_slots[2 * ATTN_MAX_WG];
   __shared__ int s_np;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int w0 = s_lo >> 1, nw = (s_hi >> 1) - w0 + 1;
+  if (tid < 64) {
+    const int lane = tid;
     int n = 0;
-    for (int k0 = 0; k0 < nw; k0 += 64) {
-      const int k = k0 + lane;
-      int sl = -1;
-      if (k < nw) sl = (k == 0) ? s_lo : 2 * (w0 + k);
-      const bool ok = sl >= 0 && a.part_tag[sl] == item;
+    for (int k0 = w0; k0 <= w1; k0 += 64) {
+      const int w = k0 + lane;
+      const int lo = range_lo(w, T, W), hi = range_lo(w + 1, T, W);
+      const bool ok = w <= w1 && max(lo, istart) < min(hi, iend);
       const unsigned long long bal = __ballot(ok);
-      if (ok) s_slots[n + __popcll(bal & ((1ull << lane) - 1))] = sl;
+      if (ok) s_slots[n + __popcll(bal & ((1ull << lane) - 1))] = 2 * w + (lo < c0 ? 1 : 0);
       n += __popcll(bal);
     }
     if (lane == 0) s_np = n;
@@ -517,6 +529,60 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const Att
   constexpr int KB = 4;                      // pieces per batch of loads
   const int nitems = RG * (D / 4);           // output elements of 4 dims
   __shared__ float s_m[CHUNK][64], s_l[CHUNK][64], s_f[CHUNK][64], s_M[64], s_inv[64];
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (np <= KB && nitems <= PER * COMBINE_THREADS) {
+    // Few pieces, one pass: the O values of every piece and the (m, l) pairs go out in
+    // one round trip; the weights follow from LDS.  Same arithmetic as the general path.
+    f32x4 ov[PER][KB];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int it = min(e * COMBINE_THREADS + (int)threadIdx.x, nitems - 1);
+      const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        ov[e][k] = *reinterpret_cast<const f32x4*>(a.part_o + ((size_t)slot_of(min(k, np - 1)) * RG + qr) * D + 4 * d4);
+    }
+    {
+      const int k = threadIdx.x >> 6, qr = threadIdx.x & 63;  // COMBINE_THREADS = KB * 64
+      const float* ml = a.part_ml + ((size_t)slot_of(min(k, np - 1)) * RG + min(qr, RG - 1)) * 2;
+      const float m = ml[0], l = ml[1];
+      s_m[k][qr] = m;
+      s_l[k][qr] = l;
+    }
+    lds_barrier();
+    for (int qr = threadIdx.x; qr < RG; qr += COMBINE_THREADS) {
+      float M = neg_inf();
+      for (int k = 0; k < np; ++k) M = fmaxf(M, s_m[k][qr]);
+      float den = 0.f;
+      for (int k = 0; k < np; ++k) {
+        const float m = s_m[k][qr];
+        den += ((m == neg_inf()) ? 0.f : exp2_hw(m - M)) * s_l[k][qr];
+      }
+      s_inv[qr] = 1.f / den;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const float m = s_m[k][qr];
+        s_f[k][qr] = (k < np && m != neg_inf()) ? exp2_hw(m - M) : 0.f;
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int it = e * COMBINE_THREADS + threadIdx.x;
+      if (it >= nitems) break;
+      const int qr = it / (D / 4), d4 = it - qr * (D / 4);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KB; ++k) acc += s_f[k][qr] * ov[e][k];
+      const float inv = s_inv[qr];
+      const int r = qr / G, hg = qr - r * G;
+      u32x2 wv;
+      wv[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+      wv[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 4 * d4) = wv;
+    }
+    return;
+  }
   if (np <= CHUNK) {
     for (int idx = threadIdx.x; idx < np * 64; idx += COMBINE_THREADS) {
       const int k = idx >> 6, qr = idx & 63;
@@ -545,7 +611,6 @@ __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const Att
     s_M[qr] = M;
     s_inv[qr] = 1.f / den;
   }
-  uint16_t* out = static_cast<uint16_t*>(a.out);
   for (int base = 0; base < nitems; base += PER * COMBINE_THREADS) {
     f32x4 acc[PER];
 #pragma unroll

@@ -40,7 +40,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- attention workspace
 struct AttnWs {
-  size_t part_o, part_ml, part_tag, total;
+  size_t part_o, part_ml, total;
 };
 
 AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
@@ -50,8 +50,7 @@ AttnWs attn_ws(int B, int N, int Hq, int Hkv, int D, int max_ctx_len) {
   const size_t slots = (size_t)isd::ATTN_MAX_WG * 2;
   w.part_o = 0;
   w.part_ml = align256(slots * RG * D * sizeof(float));
-  w.part_tag = w.part_ml + align256(slots * RG * 2 * sizeof(float));
-  w.total = w.part_tag + align256(slots * sizeof(int32_t));
+  w.total = w.part_ml + align256(slots * RG * 2 * sizeof(float));
   return w;
 }
 
@@ -160,7 +159,6 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   char* ws = static_cast<char*>(workspace);
   a.part_o = ws ? reinterpret_cast<float*>(ws + w.part_o) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(ws + w.part_ml) : nullptr;
-  a.part_tag = ws ? reinterpret_cast<int32_t*>(ws + w.part_tag) : nullptr;
   return hip_status(isd::launch_attention(a, static_cast<hipStream_t>(stream)), "attention launch");
 }
 

@@ -26,7 +26,6 @@ struct AttnLaunch {
   // workspace carve-up: two partial slots per workgroup of the balanced grid
   float* part_o;         // [ATTN_MAX_WG * 2][R*G][D]
   float* part_ml;        // [ATTN_MAX_WG * 2][R*G][2]
-  int32_t* part_tag;     // [ATTN_MAX_WG * 2] item (b * Hkv + kv head) held by each slot, or -1
 };
 constexpr int ATTN_MAX_WG = 2048;  // workgroups of the balanced attention grid, at most
 constexpr int ATTN_MAX_B = 2048;   // requests per bf16 attention call
