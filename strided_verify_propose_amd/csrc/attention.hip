@@ -206,7 +206,7 @@ __device__ __forceinline__ int range_lo(int w, int T, int W) {
 }
 
 template <int D, int NQB>
-__global__ __launch_bounds__(AttnShape<NQB>::THREADS, (AttnShape<NQB>::QB == 1) ? 3 : 2)
+__global__ __launch_bounds__(AttnShape<NQB>::THREADS, 2)
 void attn_bf16_kernel(const AttnLaunch a) {
   constexpr int QB = AttnShape<NQB>::QB;
   constexpr int GROUPS = AttnShape<NQB>::GROUPS;
