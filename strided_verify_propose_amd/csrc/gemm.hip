@@ -147,17 +147,33 @@ __device__ void gemm_tile(Tiles (&lds)[2], const uint16_t* __restrict__ X, int l
 __global__ __launch_bounds__(THREADS) void base_kernel(const ProjLaunch p) {
   const int mt = (p.M + BM - 1) / BM, nt = (p.Nout + p.r) / BN;
   int tm, tn;
-  if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
+  if (!tile_of(blockIdx.x, mt, nt * p.ksplit, tm, tn)) return;
+  const int ks = tn % p.ksplit, klen = p.K / p.ksplit, k0 = ks * klen;  // this part of K
+  tn /= p.ksplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, gq = lane >> 4;
   const int m0 = tm * BM, n0 = tn * BN;
   const int mrows = min(BM, p.M - m0);
   const bool lowrank = n0 >= p.Nout;  // this tile computes T = X A
-  const uint16_t* Bsrc = lowrank ? p.A + (size_t)(n0 - p.Nout) * p.K : p.W + (size_t)n0 * p.K;
+  const uint16_t* Bsrc = (lowrank ? p.A + (size_t)(n0 - p.Nout) * p.K : p.W + (size_t)n0 * p.K) + k0;
   __shared__ Tiles lds[2];
   f32x4 acc[2][4];
-  gemm_tile<PROJ_RING>(lds, p.X + (size_t)m0 * p.K, p.K, mrows, Bsrc, p.K, p.K, tid, wm, wn, lane, acc);
+  gemm_tile<PROJ_RING>(lds, p.X + (size_t)m0 * p.K + k0, p.K, mrows, Bsrc, p.K, klen, tid, wm, wn, lane, acc);
+  if (p.ksplit > 1) {  // partial sums; proj_reduce_kernel adds them in order and stores
+    const int ncols = p.Nout + p.r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm * 32 + i * 16 + 4 * gq + e;
+        if (row >= mrows) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p.part[((size_t)ks * p.M + m0 + row) * ncols + n0 + wn * 64 + j * 16 + l16] = acc[i][j][e];
+      }
+    return;
+  }
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -225,10 +241,52 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
 
 int grid_of(int M, int ncols) { return tile_grid((M + BM - 1) / BM, ncols / BN); }
 
+// Sum of the K parts, in part order, then the base kernel's stores: T for the A^T
+// columns, the fp32 base product for gated rows, bf16 for the others.  Four columns
+// per thread.
+__global__ __launch_bounds__(256) void proj_reduce_kernel(const ProjLaunch p) {
+  const int ncols = p.Nout + p.r, q4 = ncols / 4;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)p.M * q4) return;
+  const int row = (int)(idx / q4), col = (int)(idx - (long long)row * q4) * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(p.part + (size_t)row * ncols + col);
+  for (int s = 1; s < p.ksplit; ++s)
+    v += *reinterpret_cast<const f32x4*>(p.part + ((size_t)s * p.M + row) * ncols + col);
+  if (col >= p.Nout) {
+    uint16_t* t = p.T + (size_t)row * p.r + (col - p.Nout);
+    for (int i = 0; i < 4; ++i) t[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+  } else if (p.gate != nullptr && p.gate[row] != 0) {
+    *reinterpret_cast<f32x4*>(p.Ybase + (size_t)row * p.Nout + col) = v;
+  } else {
+    u32x2 w;
+    w[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    w[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(p.Y + (size_t)row * p.Nout + col) = w;
+  }
+}
+
 }  // namespace
 
+int proj_ksplit(int M, int K, int Nout) {
+  // the base tiles alone (not the A^T columns) decide, so gated and base-only calls agree
+  const int tiles = ((M + BM - 1) / BM) * (Nout / BN);
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 256 && (K / (2 * s)) % BK == 0 && K / (2 * s) >= 4 * BK) s *= 2;
+  return s;
+}
+
+hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s) {
+  const long long n = (long long)p.M * ((p.Nout + p.r) / 4);
+  proj_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s) {
-  base_kernel<<<grid_of(p.M, p.Nout + p.r), THREADS, 0, s>>>(p);
+  base_kernel<<<grid_of(p.M, (p.Nout + p.r) * p.ksplit), THREADS, 0, s>>>(p);
+  if (p.ksplit > 1) {
+    const hipError_t e = launch_proj_reduce(p, s);
+    if (e != hipSuccess) return e;
+  }
   if (p.gate) lora_kernel<<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -111,15 +111,16 @@ __device__ __forceinline__ void mma(const Frags& f, const Stage& st, f32x4 (&acc
 }
 
 // acc[rb][cb] = sum over k < K of X[16 rb + row][k] S[32 wave + 16 cb + col][k] for the
-// 64 x 128 tile at X and the packed fragments at Sp (the tile's first 16-column block).
+// 64 x 128 tile at X and the packed fragments at Sp (the tile's first 16-column block, at
+// the first k of the part; Kfull is the weights' full K).
 // X rows past `mrows` read row mrows - 1 (never stored).  At step s: loads for step
 // s + RING - 1 go out, step s + 2's activations go to LDS, step s + 1's activation
 // fragments come from LDS, and step s's MFMAs run.
 __device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int ldx, int mrows,
-                          const uint16_t* __restrict__ Sp, int K, int tid, int wave, int lane,
+                          const uint16_t* __restrict__ Sp, int Kfull, int K, int tid, int wave, int lane,
                           f32x4 (&acc)[BM / 16][2]) {
   static_assert(RING % 2 == 0 && RING >= 4, "fragment buffers alternate with the step parity");
-  const int KB = K / 32;
+  const int KB = Kfull / 32;  // fragments per 16-column block of the packed weights
   const uint16_t* pa[A_LOADS];
   const uint16_t* pb[2];
 #pragma unroll
@@ -159,7 +160,9 @@ __device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int l
 __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p) {
   const int mt = (p.M + BM - 1) / BM, nt = (p.Nout + p.r) / BN;
   int tm, tn;
-  if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
+  if (!tile_of(blockIdx.x, mt, nt * p.ksplit, tm, tn)) return;
+  const int ks = tn % p.ksplit, klen = p.K / p.ksplit, k0 = ks * klen;  // this part of K
+  tn /= p.ksplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -168,7 +171,22 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
   const size_t blk = (size_t)(p.K / 32) * FRAG;  // elements per packed 16-column block
   __shared__ ATile lds[2];
   f32x4 acc[BM / 16][2];
-  gemm_tile(lds, p.X + (size_t)m0 * p.K, p.K, mrows, p.Sp + (size_t)(n0 / 16) * blk, p.K, tid, wave, lane, acc);
+  gemm_tile(lds, p.X + (size_t)m0 * p.K + k0, p.K, mrows, p.Sp + (size_t)(n0 / 16) * blk + (size_t)(k0 / 32) * FRAG,
+            p.K, klen, tid, wave, lane, acc);
+  if (p.ksplit > 1) {  // partial sums; the reduce kernel adds them in order and stores
+    const int ncols = p.Nout + p.r;
+#pragma unroll
+    for (int rb = 0; rb < BM / 16; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rb * 16 + 4 * gq + e;
+        if (row >= mrows) continue;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          p.part[((size_t)ks * p.M + m0 + row) * ncols + n0 + wave * 32 + cb * 16 + l16] = acc[rb][cb][e];
+      }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < BM / 16; ++rb)
 #pragma unroll
@@ -195,7 +213,11 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
 
 hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s) {
   const int mt = (p.M + BM - 1) / BM;
-  base_kernel_packed<<<tile_grid(mt, (p.Nout + p.r) / BN), THREADS, 0, s>>>(p);
+  base_kernel_packed<<<tile_grid(mt, (p.Nout + p.r) / BN * p.ksplit), THREADS, 0, s>>>(p);
+  if (p.ksplit > 1) {
+    const hipError_t e = launch_proj_reduce(p, s);
+    if (e != hipSuccess) return e;
+  }
   if (p.gate) return launch_lora(p, s);  // K = r: the row-major kernel on B^T as stored
   return hipGetLastError();
 }

@@ -78,15 +78,17 @@ VerWs ver_ws(int B, int N, int V) {
 
 // ---------------------------------------------------------------- projection workspace
 struct ProjWs {
-  size_t ybase, T, total;
+  size_t ybase, T, part, total;
+  int ksplit;
 };
 
 ProjWs proj_ws(int M, int K, int Nout, int r) {
-  (void)K;
   ProjWs w{};
+  w.ksplit = isd::proj_ksplit(M, K, Nout);
   w.ybase = 0;
   w.T = align256(r > 0 ? (size_t)M * Nout * sizeof(float) : 0);
-  w.total = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
+  w.part = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
+  w.total = w.part + align256(w.ksplit > 1 ? (size_t)w.ksplit * M * (Nout + r) * sizeof(float) : 0);
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -232,7 +234,7 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
       return fail(ISD_ERR_UNSUPPORTED, "gated_lora_proj: r=%d (supported: 128, 256)", r);
   }
   const ProjWs ws_ = proj_ws(M, K, Nout, lora ? r : 0);
-  if (lora && (!workspace || workspace_bytes < ws_.total))
+  if ((lora || ws_.ksplit > 1) && (!workspace || workspace_bytes < ws_.total))
     return fail(ISD_ERR_WORKSPACE, "gated_lora_proj: workspace %zu bytes, need %zu", workspace_bytes, ws_.total);
   char* ws = static_cast<char*>(workspace);
   isd::ProjLaunch p{};
@@ -240,6 +242,8 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
   p.W = static_cast<const uint16_t*>(w);
   p.Y = static_cast<uint16_t*>(y);
   p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
+  p.ksplit = ws_.ksplit;
+  p.part = ws ? reinterpret_cast<float*>(ws + ws_.part) : nullptr;
   if (lora) {
     p.A = static_cast<const uint16_t*>(a);
     p.Bl = static_cast<const uint16_t*>(b);
@@ -300,7 +304,7 @@ isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const u
   if (gate && r == 0) return fail(ISD_ERR_INVALID_ARG, "gated_lora_proj_packed: gate given with r=0");
   const bool lora = gate != nullptr;
   const ProjWs ws_ = proj_ws(M, K, Nout, lora ? r : 0);
-  if (lora && (!workspace || workspace_bytes < ws_.total))
+  if ((lora || ws_.ksplit > 1) && (!workspace || workspace_bytes < ws_.total))
     return fail(ISD_ERR_WORKSPACE, "gated_lora_proj_packed: workspace %zu bytes, need %zu", workspace_bytes,
                 ws_.total);
   char* ws = static_cast<char*>(workspace);
@@ -310,6 +314,8 @@ isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const u
   p.Y = static_cast<uint16_t*>(y);
   p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
   p.Sp = pk;
+  p.ksplit = ws_.ksplit;
+  p.part = ws ? reinterpret_cast<float*>(ws + ws_.part) : nullptr;
   if (lora) {
     p.gate = gate;
     p.r = r;

@@ -97,9 +97,15 @@ struct ProjLaunch {
   float* Ybase;                 // workspace [M, Nout] fp32 (rows with gate 1)
   uint16_t* T;                  // workspace [M, r] bf16
   const uint16_t* Sp;           // packed path: [W^T; A^T] in fragment order
+  int ksplit;                   // K split into this many equal parts (1: none)
+  float* part;                  // workspace [ksplit][M][Nout + r] fp32 partial sums (ksplit > 1)
 };
+// K split of the projection for few tiles: a function of (M, K, Nout) only, so that a
+// gated call and the base-only call on the same x, w split -- and round -- alike.
+int proj_ksplit(int M, int K, int Nout);
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s);
 hipError_t launch_lora(const ProjLaunch& p, hipStream_t s);  // the second kernel alone
+hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s);  // sum of the K parts
 hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s);
 // Pack [W^T; A^T] (Nout + r rows of K) into fragment order and copy B^T after it.
 hipError_t launch_pack_proj(const uint16_t* w, const uint16_t* a, const uint16_t* b, uint16_t* packed,
