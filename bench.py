@@ -223,6 +223,18 @@ def main():
     p_flops = 2 * pcfg.M * pcfg.K * pcfg.Nout + 2 * m_g * pcfg.K * pcfg.r + 2 * m_g * pcfg.r * pcfg.Nout
     p_us = float(np.mean(proj_ms)) * 1e3
 
+    # measured device copy ceiling: a 512 MiB device-to-device copy, timed with events
+    src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * 5 * (1 << 29) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -259,6 +271,10 @@ def main():
         "tpf_closed_form_at_p_hat": round(tpf_closed_form(N, p_hat), 4),
         "kernels_us": {"gated_lora_proj": round(p_us, 2), "attention": round(a_us, 2),
                        "verify": round(v_us, 2)},
+        "kernels_us_p10_p50_p90": {k: [round(float(np.percentile(x, q)) * 1e3, 2) for q in (10, 50, 90)]
+                                   for k, x in (("gated_lora_proj", proj_ms), ("attention", att_ms),
+                                                ("verify", ver_ms))},
+        "device_copy_GBps": round(copy_gbps, 1),
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
         "roofline": {"bound": "hbm",
