@@ -484,19 +484,27 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
   __shared__ double s_a, s_u;
   __shared__ WalkState s_st;
 
+  __shared__ float s_uu[16];  // the request's uniforms (R <= 15)
+
   // a cold request (draft_ids[b][0] < 0) has no valid drafts
   const bool cold = N > 1 && v.draft_ids[(size_t)b * (N - 1)] < 0;
 
-  // logits at the draft ids, gathered in parallel (two dependent round trips, which the
-  // row loads below overlap)
+  // Loads issued before the row statistics below: the uniforms, and the draft ids whose
+  // logits this thread gathers (thread i < N-1: verify row i; thread 64 + i: draft row i).
+  // The gather itself goes out right after the statistics' loads, so its round trip
+  // overlaps their arithmetic instead of preceding it.
+  const float u_pre = (tid < R) ? v.u[(size_t)b * R + tid] : 0.f;
+  const T* gsrc = nullptr;
+  int gid = 0;
   if (tid < N - 1) {
-    const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + tid], 0), v.V - 1);
-    s_lp[tid] = to_f(lg[((size_t)b * R + tid) * v.V + d]);
+    gid = v.draft_ids[(size_t)b * (N - 1) + tid];
+    gsrc = lg + ((size_t)b * R + tid) * v.V;
   } else if (dl && tid >= 64 && tid < 64 + N - 1) {
-    const int i = tid - 64;
-    const int d = min(max(v.draft_ids[(size_t)b * (N - 1) + i], 0), v.V - 1);
-    s_lq[i] = to_f(dl[((size_t)b * (N - 1) + i) * v.V + d]);
+    gid = v.draft_ids[(size_t)b * (N - 1) + (tid - 64)];
+    gsrc = dl + ((size_t)b * (N - 1) + (tid - 64)) * v.V;
   }
+  float glog = 0.f;
+  bool gathered = false;
 
   // A. per row (one wave each; the proposal rows only in the lead workgroup): raw max
   //    and its lowest id, reference Kmax, chunk factors 2^(K_c - Kmax) and
@@ -517,6 +525,12 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
 #pragma unroll
       for (int t = 0; t < CSL; ++t) cv[q][t] = v.csub[rowid * NSUB + min(t * 64 + lane, NSUB - 1)];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (gsrc && !gathered) {
+      glog = to_f(gsrc[min(max(gid, 0), v.V - 1)]);
+      gathered = true;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < RPB; ++q) {
       const int rr = r0 + q * WAVES;
@@ -558,6 +572,10 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       }
     }
   }
+  if (gsrc && !gathered) glog = to_f(gsrc[min(max(gid, 0), v.V - 1)]);
+  if (tid < N - 1) s_lp[tid] = glog;
+  else if (gsrc) s_lq[tid - 64] = glog;
+  if (tid < R) s_uu[tid] = u_pre;
   __syncthreads();
 
   // rows without statistics (no draft rows with argmax drafts) report 0
@@ -584,7 +602,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       const double a = s_ratio[i];
       uint8_t acc = 0;
       if (rej < 0) {
-        const double u = (double)v.u[(size_t)b * R + i];
+        const double u = (double)s_uu[i];
         if (u < a) {
           acc = 1;
         } else {
@@ -656,7 +674,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     int k;
     if (jb < N) {
       const int rr = N - 1 + jb;
-      const double u = (double)v.u[(size_t)b * R + rr];
+      const double u = (double)s_uu[rr];
       k = sample_row<T, VEC>(v, b, rr, s_fac[rr], u * s_Z[rr], -1, lane, stash ? s_cs + rr * NSUB : nullptr);
       if (lane == 0) {
         v.sampled_ids[(size_t)b * N + jb] = k;
@@ -665,7 +683,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
       }
     } else if (cold) {
       // no valid drafts: the exact token of the next position from row 0 at u_0
-      k = sample_row<T, VEC>(v, b, 0, s_fac[0], (double)v.u[(size_t)b * R] * s_Z[0], -1, lane,
+      k = sample_row<T, VEC>(v, b, 0, s_fac[0], (double)s_uu[0] * s_Z[0], -1, lane,
                              stash ? s_cs : nullptr);
       if (lane == 0) v.next_token[b] = k;
     } else {
