@@ -279,3 +279,78 @@ def proj_inputs(cfg: ProjConfig, seed: int | None = None, M: int | None = None) 
     pat = np.asarray(cfg.gate_pattern, np.uint8)
     gate = np.resize(pat, M).astype(np.uint8)
     return ProjInputs(cfg, x, w, a, b, gate)
+
+
+# ----------------------------------------------------------------------------- LM head
+@dataclass
+class LmHeadConfig:
+    """LM head in front of verification: hidden [B (2N-1), Dm] times w_lm [V, Dm]^T.
+
+    grid=True draws every hidden value as k/4 (k integer in [-4, 4]) and every weight as
+    k/32 (k in [-2, 2]): all products and partial sums are multiples of 2^-7 below 2^15
+    in magnitude for Dm <= 4096, so any float32 summation order gives the exact product
+    and the stored bf16 logits are unique.  grid=False draws N(0, h_sd) and N(0, w_sd)."""
+    name: str
+    B: int
+    N: int
+    Dm: int
+    V: int
+    h_sd: float
+    w_sd: float
+    draft_sd: float
+    grid: bool
+    seed: int
+
+    @property
+    def R(self) -> int:
+        return 2 * self.N - 1
+
+    @property
+    def M(self) -> int:
+        return self.B * self.R
+
+
+# Qwen3-8B's hidden size and vocabulary; weights scaled so the logits have sd ~3 like the
+# verification workload's anchors.
+LM_HEAD_8B = LmHeadConfig("lm_head_qwen3_8b_b64_n4", B=64, N=4, Dm=4096, V=151936,
+                          h_sd=1.0, w_sd=3.0 / 64.0, draft_sd=3.0, grid=False, seed=1005)
+
+
+@dataclass
+class LmHeadInputs:
+    cfg: LmHeadConfig
+    hidden: np.ndarray          # [M, Dm] bf16 bits, request-major (row b R + r)
+    w_lm: np.ndarray            # [V, Dm] bf16 bits
+    draft_logits: np.ndarray | None   # [B, N-1, V] bf16 bits (previous step's proposal rows)
+    draft_ids: np.ndarray       # [B, N-1] int32
+    uniforms: np.ndarray        # [B, 2N-1] float32
+
+
+def _grid(g: np.random.Generator, shape, kmax: int, scale: float) -> np.ndarray:
+    return (g.integers(-kmax, kmax + 1, size=shape).astype(np.float32) * np.float32(scale))
+
+
+def lm_head_inputs(cfg: LmHeadConfig, seed: int | None = None, argmax_drafts: bool = False) -> LmHeadInputs:
+    """Hidden states, output embedding, and draft rows drawn independently of the
+    product (N(0, draft_sd)); drafts are Gumbel draws from those rows, or their argmax."""
+    g = streams(cfg.seed if seed is None else seed)
+    B, N, R, V = cfg.B, cfg.N, cfg.R, cfg.V
+    if cfg.grid:
+        hidden = bf16_rne(_grid(g["x"], (cfg.M, cfg.Dm), 4, 0.25))
+        w_lm = bf16_rne(_grid(g["w"], (V, cfg.Dm), 2, 1.0 / 32.0))
+    else:
+        hidden = bf16_rne(normal(g["x"], (cfg.M, cfg.Dm), cfg.h_sd))
+        w_lm = np.empty((V, cfg.Dm), np.uint16)
+        step = 8192                                      # bounded float32 temporaries
+        for v0 in range(0, V, step):
+            w_lm[v0:v0 + step] = bf16_rne(normal(g["w"], (min(step, V - v0), cfg.Dm), cfg.w_sd))
+    draft_stored = bf16_rne(normal(g["anchor"], (B, N - 1, V), cfg.draft_sd))
+    draft_vals = bf16_bits_to_f32(draft_stored)
+    if argmax_drafts:
+        draft_ids = np.argmax(draft_vals, axis=-1).astype(np.int32)
+        draft_logits = None
+    else:
+        draft_ids = gumbel_argmax(draft_vals, g["drafts"])
+        draft_logits = draft_stored
+    u = uniforms24(g["uniforms"], (B, R))
+    return LmHeadInputs(cfg, hidden, w_lm, draft_logits, draft_ids, u)

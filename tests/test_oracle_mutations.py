@@ -86,3 +86,18 @@ def test_wrong_tpf_exponent_is_caught(monkeypatch):
         "tpf_n4_p09": {"N": 4, "p": 0.9, "value": 2.9, "decimals": 1},
         "efficiency_n4_p09": {"N": 4, "p": 0.9, "queries": 7, "value": 1.22, "decimals": 2},
         "queries_per_forward_n4": {"value": 7}})
+
+
+def test_lm_head_without_rounding_is_caught(monkeypatch):
+    import oracle.lm_head as olm
+    from tests import test_oracle_lm_head as t_lm
+    monkeypatch.setattr(olm, "round_bf16", lambda x: x)
+    fails(t_lm.test_grid_inputs_give_the_exact_product_rounded_to_bf16)
+
+
+def test_lm_head_wrong_weight_column_is_caught(monkeypatch):
+    import oracle.lm_head as olm
+    from tests import test_oracle_lm_head as t_lm
+    monkeypatch.setattr(olm, "lm_head_logits",
+                        lambda h, w: olm.round_bf16(olm.to_f64(h) @ np.roll(olm.to_f64(w), 1, axis=1).T))
+    fails(t_lm.test_one_hot_rows_pick_one_weight_each)
