@@ -10,6 +10,10 @@
  *   isd_gated_lora_proj  R-ISD projection: base weights on every row, LoRA delta on gated rows
  *                        (also on weights packed once in MMA fragment order: *_packed)
  *
+ * and, around them, isd_commit (what a step keeps, for a loop that stays on the device)
+ * and isd_lm_head / isd_lm_head_verify (the vocabulary projection that produces the
+ * logits rows, alone or fused with verification's row pass).
+ *
  * Conventions for every entry point
  *   - Tensor arguments are DEVICE pointers, dense and row-major in the shapes given, owned
  *     by the caller.  The library allocates nothing and keeps no state between calls.
@@ -194,6 +198,39 @@ isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, vo
 isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const uint8_t* gate,
                                       void* y, int M, int K, int Nout, int r, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- LM head
+ * The vocabulary projection that turns the block's 2N-1 rows into the logits rows that
+ * verification reads: anchors on the clean rows, proposals on the [MASK] rows, from one
+ * forward (「首次超越 AR 模型」 "I-DLM 如何解決這些問題"; 「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD").
+ * bf16 only; fp32 accumulation.
+ *   hidden  [M, Dm] bf16: final hidden states of the block rows, request-major (row
+ *           b (2N-1) + r is row r of request b)
+ *   w_lm    [V, Dm] bf16: the output embedding, one row of Dm weights per vocabulary entry
+ *   logits  [M, V] bf16 out (= [B, 2N-1, V]): the fp32-accumulated product hidden . w_lm^T
+ *           rounded to the nearest bf16, ties to even
+ * isd_lm_head: the logits alone; no workspace.
+ *   Requires: Dm % 32 == 0 (32 <= Dm <= 65536), V % 8 == 0 (8 <= V <= 2^20),
+ *   1 <= M <= 65536.
+ * isd_lm_head_verify: the logits, and verification of them in the same pass: the row
+ *   statistics of the logits rows (max, lowest argmax, sums of exponentials per 1024
+ *   entries) come from each output tile before it leaves the chip, so the logits rows are
+ *   written once and read back only where a draw or the residual needs them.  M = B (2N-1).
+ *   Arguments from draft_logits on, and every output, are isd_verify's with dt = ISD_BF16
+ *   and logits = the stored logits: argmax ids are identical; P, Q, row_lse and the draws
+ *   agree with isd_verify on the same logits up to float rounding (the sums are added in
+ *   another order), so an id can differ only where a uniform lies within that rounding of
+ *   a boundary.  Requires the above and 1 <= N <= 8, 1 <= B <= 65535, temperature > 0.
+ *   Workspace: isd_lm_head_verify_workspace_bytes(B, N, V). */
+isd_status isd_lm_head(const void* hidden, const void* w_lm, void* logits, int M, int Dm, int V,
+                       void* stream);
+size_t isd_lm_head_verify_workspace_bytes(int B, int N, int V);
+isd_status isd_lm_head_verify(const void* hidden, const void* w_lm, void* logits,
+                              const void* draft_logits, const int32_t* draft_ids, const float* uniforms,
+                              int B, int N, int Dm, int V, float temperature, int32_t* n_accept,
+                              uint8_t* accept, int32_t* next_token, int32_t* argmax_ids,
+                              int32_t* sampled_ids, float* p_draft, float* q_draft, float* row_lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -76,6 +76,26 @@ VerWs ver_ws(int B, int N, int V) {
   return w;
 }
 
+// ---------------------------------------------------------------- LM-head workspace
+// The verification's records, then the LM head's mini-chunk records of the logits rows.
+struct LmhWs {
+  VerWs v;
+  int NMINI;
+  size_t mmax, msum, marg, total;
+};
+
+LmhWs lmh_ws(int B, int N, int V) {
+  LmhWs w{};
+  w.v = ver_ws(B, N, V);
+  w.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
+  const size_t recs = (size_t)B * (2 * N - 1) * w.NMINI;
+  w.mmax = w.v.total;
+  w.msum = w.mmax + align256(recs * sizeof(float));
+  w.marg = w.msum + align256(recs * sizeof(float));
+  w.total = w.marg + align256(recs * sizeof(int32_t));
+  return w;
+}
+
 // ---------------------------------------------------------------- projection workspace
 struct ProjWs {
   size_t ybase, T, part, total;
@@ -91,6 +111,34 @@ ProjWs proj_ws(int M, int K, int Nout, int r) {
   w.total = w.part + align256(w.ksplit > 1 ? (size_t)w.ksplit * M * (Nout + r) * sizeof(float) : 0);
   if (w.total == 0) w.total = 256;
   return w;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- LM head
+namespace {
+
+isd_status check_lm_head(const char* who, const void* hidden, const void* w_lm, const void* logits,
+                         long long M, int Dm, int V) {
+  if (!hidden || !w_lm || !logits) return fail(ISD_ERR_INVALID_ARG, "%s: null tensor pointer", who);
+  if (M < 1 || M > 65536) return fail(ISD_ERR_INVALID_ARG, "%s: %lld rows out of [1, 65536]", who, M);
+  if (Dm < 32 || Dm > 65536 || Dm % 32)
+    return fail(ISD_ERR_UNSUPPORTED, "%s: Dm=%d (multiple of 32 in [32, 65536] required)", who, Dm);
+  if (V < 8 || V > (1 << 20) || V % 8)
+    return fail(ISD_ERR_UNSUPPORTED, "%s: V=%d (multiple of 8 in [8, 2^20] required)", who, V);
+  return ISD_OK;
+}
+
+isd::LmhLaunch lmh_launch(const void* hidden, const void* w_lm, void* logits, int M, int Dm, int V,
+                          float c2) {
+  isd::LmhLaunch p{};
+  p.hidden = static_cast<const uint16_t*>(hidden);
+  p.w = static_cast<const uint16_t*>(w_lm);
+  p.logits = static_cast<uint16_t*>(logits);
+  p.M = M; p.Dm = Dm; p.V = V;
+  p.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
+  p.c2 = c2;
+  return p;
 }
 
 }  // namespace
@@ -198,6 +246,7 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
   v.B = B; v.N = N; v.R = 2 * N - 1;
   v.RR = v.R + (v.draft ? N - 1 : 0);
   v.V = V; v.SV = w.SV; v.NSUB = w.NSUB;
+  v.srow0 = 0; v.snrow = v.RR;
   v.invT = 1.f / temperature;
   v.c2 = (float)(1.4426950408889634 / (double)temperature);
   v.n_accept = n_accept; v.accept = accept; v.next_token = next_token;
@@ -324,6 +373,80 @@ isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const u
     p.T = reinterpret_cast<uint16_t*>(ws + ws_.T);
   }
   return hip_status(isd::launch_proj_packed(p, static_cast<hipStream_t>(stream)), "gated_lora_proj_packed launch");
+}
+
+
+
+isd_status isd_lm_head(const void* hidden, const void* w_lm, void* logits, int M, int Dm, int V,
+                       void* stream) {
+  const isd_status st = check_lm_head("lm_head", hidden, w_lm, logits, M, Dm, V);
+  if (st != ISD_OK) return st;
+  const isd::LmhLaunch p = lmh_launch(hidden, w_lm, logits, M, Dm, V, 1.f);
+  return hip_status(isd::launch_lm_head(p, static_cast<hipStream_t>(stream)), "lm_head launch");
+}
+
+size_t isd_lm_head_verify_workspace_bytes(int B, int N, int V) {
+  if (B < 1 || N < 1 || N > 8 || V < 8) return 0;
+  return lmh_ws(B, N, V).total;
+}
+
+isd_status isd_lm_head_verify(const void* hidden, const void* w_lm, void* logits,
+                              const void* draft_logits, const int32_t* draft_ids, const float* uniforms,
+                              int B, int N, int Dm, int V, float temperature, int32_t* n_accept,
+                              uint8_t* accept, int32_t* next_token, int32_t* argmax_ids,
+                              int32_t* sampled_ids, float* p_draft, float* q_draft, float* row_lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || B > 65535) return fail(ISD_ERR_INVALID_ARG, "lm_head_verify: B=%d out of [1, 65535]", B);
+  if (N < 1 || N > 8) return fail(ISD_ERR_UNSUPPORTED, "lm_head_verify: N=%d (supported: 1..8)", N);
+  const int R = 2 * N - 1;
+  const isd_status st = check_lm_head("lm_head_verify", hidden, w_lm, logits, (long long)B * R, Dm, V);
+  if (st != ISD_OK) return st;
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(ISD_ERR_INVALID_ARG, "lm_head_verify: temperature must be finite and > 0");
+  if (!uniforms || !n_accept || !next_token || !argmax_ids || !sampled_ids)
+    return fail(ISD_ERR_INVALID_ARG, "lm_head_verify: null tensor pointer");
+  if (N > 1 && (!draft_ids || !accept))
+    return fail(ISD_ERR_INVALID_ARG, "lm_head_verify: draft_ids and accept are required when N > 1");
+  const LmhWs w = lmh_ws(B, N, V);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(ISD_ERR_WORKSPACE, "lm_head_verify: workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  char* ws = static_cast<char*>(workspace);
+
+  isd::VerifyLaunch v{};
+  v.dtype = 1;
+  v.logits = logits;
+  v.draft = (N > 1) ? draft_logits : nullptr;
+  v.draft_ids = draft_ids; v.u = uniforms;
+  v.B = B; v.N = N; v.R = R;
+  v.RR = R + (v.draft ? N - 1 : 0);
+  v.V = V; v.SV = w.v.SV; v.NSUB = w.v.NSUB;
+  v.srow0 = R; v.snrow = N - 1;  // the stats pass covers the draft rows only
+  v.invT = 1.f / temperature;
+  v.c2 = (float)(1.4426950408889634 / (double)temperature);
+  v.n_accept = n_accept; v.accept = accept; v.next_token = next_token;
+  v.argmax_ids = argmax_ids; v.sampled_ids = sampled_ids;
+  v.p_draft = p_draft; v.q_draft = q_draft; v.row_lse = row_lse;
+  v.cmax = reinterpret_cast<float*>(ws + w.v.cmax);
+  v.cref = reinterpret_cast<float*>(ws + w.v.cref);
+  v.cidx = reinterpret_cast<int32_t*>(ws + w.v.cidx);
+  v.csub = reinterpret_cast<float*>(ws + w.v.csub);
+  v.ws = reinterpret_cast<isd::WalkState*>(ws + w.v.ws);
+  v.rsub = reinterpret_cast<float*>(ws + w.v.rsub);
+
+  isd::LmhLaunch p = lmh_launch(hidden, w_lm, logits, B * R, Dm, V, v.c2);
+  p.mmax = reinterpret_cast<float*>(ws + w.mmax);
+  p.msum = reinterpret_cast<float*>(ws + w.msum);
+  p.marg = reinterpret_cast<int32_t*>(ws + w.marg);
+  p.N = N; p.R = R; p.RR = v.RR; p.SV = v.SV; p.NSUB = v.NSUB;
+  p.cmax = v.cmax; p.cref = v.cref; p.cidx = v.cidx; p.csub = v.csub;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (v.draft) e = isd::launch_verify_stats(v, s);
+  if (e == hipSuccess) e = isd::launch_lm_head(p, s);
+  if (e == hipSuccess) e = isd::launch_lm_head_merge(p, s);
+  if (e == hipSuccess) e = isd::launch_verify_tail(v, s);
+  return hip_status(e, "lm_head_verify launch");
 }
 
 }  // extern "C"

@@ -53,6 +53,7 @@ struct VerifyLaunch {
   const int32_t* draft_ids;
   const float* u;
   int B, N, R, RR, V, SV, NSUB;
+  int srow0, snrow;             // rows srow0 .. srow0 + snrow - 1 of each request get the stats pass
   float invT, c2;               // 1/T and log2(e)/T
   int32_t* n_accept;
   uint8_t* accept;
@@ -70,7 +71,32 @@ struct VerifyLaunch {
   WalkState* ws;                // [B]
   float* rsub;                  // [B][NSUB] residual mass per sub-chunk
 };
-hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);
+hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);        // stats + tail
+hipError_t launch_verify_stats(const VerifyLaunch& v, hipStream_t s);  // the stats pass alone
+hipError_t launch_verify_tail(const VerifyLaunch& v, hipStream_t s);   // walk, residual, draws
+
+// ---------------------------------------------------------------- LM head
+constexpr int LMH_BM = 448;     // rows per LM-head workgroup (4 waves of 112)
+constexpr int LMH_BN = 128;     // vocabulary columns per LM-head workgroup (one mini-chunk)
+
+struct LmhLaunch {
+  const uint16_t* hidden;       // [M, Dm] bf16, row b R + r
+  const uint16_t* w;            // [V, Dm] bf16
+  uint16_t* logits;             // [M, V] bf16 out
+  int M, Dm, V, NMINI;          // NMINI = ceil(V / LMH_BN)
+  float c2;                     // log2(e)/T
+  float* mmax;                  // [M][NMINI] mini-chunk max; null: logits only
+  float* msum;                  // [M][NMINI] sum 2^(l c2 - fp32(max c2))
+  int32_t* marg;                // [M][NMINI] lowest column holding the max
+  // merge into the verification's records (rows b RR + r, r < R)
+  int N, R, RR, SV, NSUB;
+  float* cmax;
+  float* cref;
+  int32_t* cidx;
+  float* csub;
+};
+hipError_t launch_lm_head(const LmhLaunch& p, hipStream_t s);        // logits (+ mini-chunk records)
+hipError_t launch_lm_head_merge(const LmhLaunch& p, hipStream_t s);  // records -> chunk records
 
 // ---------------------------------------------------------------- commit
 struct CommitLaunch {

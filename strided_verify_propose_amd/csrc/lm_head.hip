@@ -1,0 +1,278 @@
+// LM head in front of verification (bf16): logits = hidden . w_lm^T, stored as bf16, with
+// the verification's row statistics taken from the tile while it is still on chip.
+//
+// One ISD forward yields the anchor p on the clean rows and the proposal q on the [MASK]
+// rows from the same block of 2N-1 rows (「首次超越 AR 模型」 "I-DLM 如何解決這些問題";
+// 「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD"); the vocabulary
+// projection that produces those rows is this product.
+//
+// lmh_kernel   One workgroup per 448-row x 128-column tile; wave w owns rows
+//              (4 x 112) x (2 x 64) over 8 waves, two per SIMD, each wave 7 x 4 blocks of
+//              v_mfma_f32_16x16x32_bf16.  Both operands are K-contiguous (hidden rows, w_lm
+//              rows), so a k step of 32 is 36 MFMA fragments of 16 rows x 64 bytes (28 of
+//              hidden, 8 of w_lm), which the waves load straight into LDS in fragment order
+//              (global_load_lds_dwordx4: lane l's 16 bytes land at slot l, which is lane
+//              l's MFMA operand, so the operand reads are conflict-free).  A ring of RING
+//              such slots keeps RING - 1 steps of loads in flight; one barrier per step.
+//              The epilogue rounds the tile to bf16 (nearest even), passes it through LDS so
+//              that every lane stores 32 contiguous bytes of a row, and -- when statistics are
+//              asked for -- reduces each row's 128 values to a mini-chunk record: the max m of
+//              the stored values, the lowest column holding it, and the sum of
+//              2^(l c2 - K) with K = fp32(m c2).
+// lmh_merge_kernel  One wave per row: mini-chunk records -> the verification's chunk
+//              records (16384 columns: max, lowest argmax, K = fp32(max c2)) and sub-chunk
+//              sums (1024 columns) against the chunk's K, rescaled and added in fp64 in
+//              column order.  The walk, residual and draw kernels then run unchanged.
+#include <limits.h>
+
+#include "device.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace isd {
+namespace {
+
+constexpr int WAVES = 8;
+constexpr int THREADS = WAVES * 64;
+constexpr int WM = LMH_BM / 4;      // 112 rows per wave (waves 4 in M x 2 in N)
+constexpr int WN = LMH_BN / 2;      // 64 columns per wave
+constexpr int BN = LMH_BN;          // 128 columns per workgroup
+constexpr int RB = WM / 16;         // 7 row blocks per wave
+constexpr int CB = WN / 16;         // 4 column blocks per wave
+constexpr int AF = LMH_BM / 16;     // 28 hidden fragments per k step
+constexpr int BF = BN / 16;         // 8 w_lm fragments per k step
+constexpr int NF = AF + BF;         // 36 fragments (1 KB each) per k step
+constexpr int LPW = (NF + WAVES - 1) / WAVES;  // loads per wave per step: 5 (waves 0..3), 4 (4..7)
+constexpr int RING = 4;             // LDS slots: RING - 1 k steps of loads in flight
+constexpr int SLOT = NF * 1024;     // bytes per slot
+constexpr int LROW = BN + 8;        // LDS row stride of the epilogue tile, in bf16
+static_assert(LMH_BM % 64 == 0 && BN == 128, "tile shape");
+static_assert(NF - (LPW - 1) * WAVES == WAVES / 2, "waves 0..3 take one more fragment than 4..7");
+static_assert(VCHUNK % BN == 0 && VSUB % BN == 0, "mini-chunks tile the chunks");
+static_assert((size_t)LMH_BM * LROW * 2 <= (size_t)RING * SLOT, "the epilogue tile fits in the ring");
+
+// s_waitcnt with only the vector-memory count bounded (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void load_frag(const uint16_t* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
+  const int mt = (p.M + LMH_BM - 1) / LMH_BM, nt = p.NMINI;
+  int tm, tn;
+  if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, kq = 8 * (lane >> 4);
+  const int m0 = tm * LMH_BM, n0 = tn * BN;
+  const int S = p.Dm / 32;
+
+  // LDS: RING slots of NF fragments during the K loop, then the bf16 output tile.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RING * SLOT];
+
+  // This wave's fragment loads: fragment f = wave + 8 i (i < LPW, f < NF); f < AF is
+  // hidden row block f, else w_lm block f - AF.  Rows past M read row M-1 and columns
+  // past V read row V-1 of w_lm (in bounds; never stored).
+  const uint16_t* src[LPW];
+  int dst[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int f = min(wave + WAVES * i, NF - 1);
+    src[i] = f < AF ? p.hidden + (size_t)min(m0 + 16 * f + l16, p.M - 1) * p.Dm + kq
+                    : p.w + (size_t)min(n0 + 16 * (f - AF) + l16, p.V - 1) * p.Dm + kq;
+    dst[i] = f * 1024;
+  }
+  const bool extra = wave < NF - (LPW - 1) * WAVES;  // this wave has an LPW-th fragment
+  auto issue = [&](int step) {
+    unsigned char* slot = smem + (step % RING) * SLOT;
+    const int k = 32 * min(step, S - 1);  // steps past the end re-load the last (dead slots)
+#pragma unroll
+    for (int i = 0; i < LPW - 1; ++i) load_frag(src[i] + k, slot + dst[i]);
+    if (extra) load_frag(src[LPW - 1] + k, slot + dst[LPW - 1]);
+  };
+
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Step s: wait until this wave's loads of step s have landed (steps s + 1 .. s + RING - 2
+  // may still be in flight), barrier (every wave's step-s fragments are in, and every wave
+  // is done with step s - 1's slot), then load step s + RING - 1 into that slot and run
+  // step s from LDS.
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) issue(u);
+  for (int s = 0; s < S; ++s) {
+    if (extra) wait_vmcnt<(RING - 2) * LPW>();
+    else wait_vmcnt<(RING - 2) * (LPW - 1)>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    issue(s + RING - 1);
+    const u32x4* fr = reinterpret_cast<const u32x4*>(smem + (s % RING) * SLOT);
+    u32x4 a[RB], b[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) b[j] = fr[(AF + CB * wn + j) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) a[i] = fr[(RB * wm + i) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // the ring is dead: reuse it as the output tile
+
+  // ---- epilogue: bf16 tile through LDS, coalesced stores, mini-chunk records
+  uint16_t(*t)[LROW] = reinterpret_cast<uint16_t(*)[LROW]>(smem);
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        t[WM * wm + 16 * i + 4 * (lane >> 4) + e][WN * wn + 16 * j + l16] =
+            (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+  __syncthreads();
+
+  // wave w: tile rows 56 w .. 56 w + 55, eight lanes per row (16 columns each)
+  constexpr int RPW = LMH_BM / WAVES;
+  const int q = lane & 7;
+  const float c2 = p.c2;
+  for (int pass = 0; pass < RPW / 8; ++pass) {
+    const int rl = RPW * wave + 8 * pass + (lane >> 3);
+    const int row = m0 + rl;
+    const int cbase = n0 + 16 * q;
+    u32x4 w2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) w2[h] = *reinterpret_cast<const u32x4*>(&t[rl][16 * q + 8 * h]);
+    if (row < p.M) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c0 = cbase + 8 * h;  // V % 8 == 0: a 16-byte group is all in or all out
+        if (c0 < p.V) *reinterpret_cast<u32x4*>(p.logits + (size_t)row * p.V + c0) = w2[h];
+      }
+    }
+    if (!p.mmax) continue;
+    float x[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * h + 2 * e] = bf16_lo(w2[h][e]);
+        x[8 * h + 2 * e + 1] = bf16_hi(w2[h][e]);
+      }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (cbase + k >= p.V) x[k] = -__builtin_inff();
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, x[k]);
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    const float K = __fmul_rn(m, c2);
+    int arg = INT_MAX;
+#pragma unroll
+    for (int k = 15; k >= 0; --k)
+      if (x[k] == m) arg = cbase + k;
+    arg = min(arg, __shfl_xor(arg, 1));
+    arg = min(arg, __shfl_xor(arg, 2));
+    arg = min(arg, __shfl_xor(arg, 4));
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sum += exp2_hw(fmaf(x[k], c2, -K));
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (q == 0 && row < p.M) {
+      const size_t o = (size_t)row * p.NMINI + tn;
+      p.mmax[o] = m;
+      p.msum[o] = sum;
+      p.marg[o] = arg;
+    }
+  }
+}
+
+// One wave per logits row m = b R + rr (rr < R): mini-chunk records -> chunk records and
+// sub-chunk sums at verification row b RR + rr.  Lane l of round t takes sub-chunk
+// 64 t + l; the 16 lanes of a 16-lane group are the 16 sub-chunks of one chunk.
+__global__ __launch_bounds__(256) void lmh_merge_kernel(const LmhLaunch p) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= p.M) return;
+  const int b = m / p.R, rr = m - b * p.R;
+  const size_t rowid = (size_t)b * p.RR + rr;
+  const bool proposal = rr >= p.N - 1;
+  const float c2 = p.c2;
+  const float* mm = p.mmax + (size_t)m * p.NMINI;
+  const float* ms = p.msum + (size_t)m * p.NMINI;
+  const int32_t* ma = p.marg + (size_t)m * p.NMINI;
+  constexpr int MPS = VSUB / BN;  // mini-chunks per sub-chunk
+  for (int j0 = 0; j0 < p.NSUB; j0 += 64) {
+    const int j = j0 + lane;
+    const bool valid = j < p.NSUB;
+    float mt[MPS], stt[MPS];
+    int at[MPS];
+#pragma unroll
+    for (int t = 0; t < MPS; ++t) {
+      const int idx = j * MPS + t;
+      const bool ok = valid && idx < p.NMINI;
+      const int ci = ok ? idx : 0;
+      mt[t] = ok ? mm[ci] : -__builtin_inff();
+      stt[t] = ok ? ms[ci] : 0.f;
+      at[t] = ok ? ma[ci] : INT_MAX;
+    }
+    float sm = -__builtin_inff();
+    int sa = INT_MAX;
+#pragma unroll
+    for (int t = 0; t < MPS; ++t)
+      if (mt[t] > sm) {  // strictly greater: ties keep the lower column
+        sm = mt[t];
+        sa = at[t];
+      }
+    float M = sm;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    int A = (sm == M) ? sa : INT_MAX;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) A = min(A, __shfl_xor(A, o));
+    const float Kc = __fmul_rn(M, c2);
+    double acc = 0.0;
+#pragma unroll
+    for (int t = 0; t < MPS; ++t)
+      if (mt[t] > -__builtin_inff())
+        acc += (double)stt[t] * exp2((double)__fmul_rn(mt[t], c2) - (double)Kc);
+    if (valid) {
+      p.csub[rowid * p.NSUB + j] = (float)acc;
+      if ((lane & 15) == 0) {
+        const int c = j / VCHUNK_SUBS;
+        p.cmax[rowid * p.SV + c] = M;
+        p.cref[rowid * p.SV + c] = Kc;
+        p.cidx[rowid * p.SV + c] = proposal ? A : INT_MAX;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lm_head(const LmhLaunch& p, hipStream_t s) {
+  const int mt = (p.M + LMH_BM - 1) / LMH_BM;
+  lmh_kernel<<<tile_grid(mt, p.NMINI), THREADS, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_head_merge(const LmhLaunch& p, hipStream_t s) {
+  lmh_merge_kernel<<<(p.M + 3) / 4, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace isd

@@ -132,7 +132,7 @@ __device__ __forceinline__ void sub_sums(const float (&s)[ROUNDS], float* lds, f
 template <typename T, bool VEC>
 __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
   constexpr int VE = VecOf<T>::n;
-  const int chunk = blockIdx.x, rr = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x, rr = v.srow0 + blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = chunk * VCHUNK;
   const T* __restrict__ row = row_ptr<T>(v, b, rr);
@@ -183,6 +183,14 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
 // The same statistics with 16-byte aligned rows, from a resident grid: workgroup w takes
 // the (row, chunk) units w, w + W, ... and keeps the next unit's loads in flight while it
 // reduces the current one.  Units are numbered (b RR + rr) SV + chunk.
+// Unit -> (request, row, chunk): units are numbered (b snrow + (rr - srow0)) SV + chunk.
+__device__ __forceinline__ void decode_unit(const VerifyLaunch& v, int unit, int& b, int& rr, int& chunk) {
+  const int rl = unit / v.SV;
+  chunk = unit - rl * v.SV;
+  b = rl / v.snrow;
+  rr = v.srow0 + (rl - b * v.snrow);
+}
+
 template <typename T>
 struct RawChunk {
   u32x4 w[kRounds<T>];  // thread t, round k: 16 bytes at base + k THREADS VE + t VE
@@ -191,8 +199,8 @@ struct RawChunk {
 template <typename T>
 __device__ __forceinline__ void load_raw(const VerifyLaunch& v, int unit, int tid, RawChunk<T>& r) {
   constexpr int VE = VecOf<T>::n;
-  const int rowid = unit / v.SV, chunk = unit - rowid * v.SV;
-  const int b = rowid / v.RR, rr = rowid - b * v.RR;
+  int b, rr, chunk;
+  decode_unit(v, unit, b, rr, chunk);
   const T* __restrict__ row = row_ptr<T>(v, b, rr);
   const int base = chunk * VCHUNK;
 #pragma unroll
@@ -209,8 +217,9 @@ __device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, i
   constexpr int VE = VecOf<T>::n;
   constexpr int NE = VCHUNK / THREADS;
   const int lane = tid & 63, wave = tid >> 6;
-  const int rowid = unit / v.SV, chunk = unit - rowid * v.SV;
-  const int rr = rowid - (rowid / v.RR) * v.RR;
+  int b, rr, chunk;
+  decode_unit(v, unit, b, rr, chunk);
+  const int rowid = b * v.RR + rr;
   const int base = chunk * VCHUNK;
   float x[NE];
 #pragma unroll
@@ -763,9 +772,9 @@ __global__ __launch_bounds__(64) void locate_kernel(const VerifyLaunch v) {
 }
 
 template <typename T>
-hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
+hipError_t launch_stats_typed(const VerifyLaunch& v, hipStream_t s) {
   const bool vec = ((size_t)v.V * sizeof(T)) % 16 == 0;
-  const dim3 g1(v.SV, v.RR, v.B);
+  const dim3 g1(v.SV, v.snrow, v.B);
   if (vec) {
     // a resident grid: a few workgroups per CU, each streaming its units
     static std::atomic<int> slots_of_device[64];
@@ -782,11 +791,17 @@ hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
       slots = max(1, per_cu) * max(1, cus);
       if (dev >= 0 && dev < 64) slots_of_device[dev].store(slots, std::memory_order_relaxed);
     }
-    const int U = v.B * v.RR * v.SV;
+    const int U = v.B * v.snrow * v.SV;
     stats_resident_kernel<T><<<min(U, slots), THREADS, 0, s>>>(v, U);
   } else {
     stats_kernel<T, false><<<g1, THREADS, 0, s>>>(v);
   }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_tail_typed(const VerifyLaunch& v, hipStream_t s) {
+  const bool vec = ((size_t)v.V * sizeof(T)) % 16 == 0;
   const dim3 g2(v.draft ? (v.NSUB + VCHUNK_SUBS / RSPLIT - 1) / (VCHUNK_SUBS / RSPLIT) + 1 : 1, v.B);
   if (vec) walk_residual_kernel<T, true><<<g2, THREADS, 0, s>>>(v);
   else walk_residual_kernel<T, false><<<g2, THREADS, 0, s>>>(v);
@@ -799,9 +814,21 @@ hipError_t launch_typed(const VerifyLaunch& v, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s) {
+hipError_t launch_verify_stats(const VerifyLaunch& v, hipStream_t s) {
+  if (v.SV > MAX_SV || v.RR > MAX_RR || v.srow0 < 0 || v.snrow < 1 || v.srow0 + v.snrow > v.RR)
+    return hipErrorInvalidValue;
+  return v.dtype == 1 ? launch_stats_typed<uint16_t>(v, s) : launch_stats_typed<float>(v, s);
+}
+
+hipError_t launch_verify_tail(const VerifyLaunch& v, hipStream_t s) {
   if (v.SV > MAX_SV || v.RR > MAX_RR) return hipErrorInvalidValue;
-  return v.dtype == 1 ? launch_typed<uint16_t>(v, s) : launch_typed<float>(v, s);
+  return v.dtype == 1 ? launch_tail_typed<uint16_t>(v, s) : launch_tail_typed<float>(v, s);
+}
+
+hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s) {
+  const hipError_t e = launch_verify_stats(v, s);
+  if (e != hipSuccess) return e;
+  return launch_verify_tail(v, s);
 }
 
 }  // namespace isd

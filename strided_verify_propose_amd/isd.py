@@ -26,7 +26,8 @@ EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_verify_workspace_bytes", "isd_verify",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
            "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed",
-           "isd_commit")
+           "isd_commit", "isd_lm_head", "isd_lm_head_verify_workspace_bytes",
+           "isd_lm_head_verify")
 
 
 class IsdError(RuntimeError):
@@ -68,6 +69,12 @@ def lib() -> ctypes.CDLL:
     L.isd_gated_lora_proj_packed.argtypes = [vp] * 4 + [i32] * 4 + [vp, sz, vp]
     L.isd_commit.restype = ctypes.c_int
     L.isd_commit.argtypes = [vp] * 7 + [i32] * 2 + [vp]
+    L.isd_lm_head.restype = i32
+    L.isd_lm_head.argtypes = [vp] * 3 + [i32] * 3 + [vp]
+    L.isd_lm_head_verify_workspace_bytes.restype = sz
+    L.isd_lm_head_verify_workspace_bytes.argtypes = [i32] * 3
+    L.isd_lm_head_verify.restype = i32
+    L.isd_lm_head_verify.argtypes = [vp] * 6 + [i32] * 4 + [f32] + [vp] * 8 + [vp, sz, vp]
     if L.isd_abi_version() != 1:
         raise RuntimeError("libisd.so ABI version mismatch")
     _lib = L
@@ -294,3 +301,61 @@ def gated_lora_proj_packed(x, packed: PackedProj, gate=None, out=None):
                                         _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
+
+
+def lm_head(hidden, w_lm, out=None):
+    """logits [M, V] bf16 = hidden [M, Dm] . w_lm [V, Dm]^T (fp32 accumulation, nearest bf16)."""
+    M, Dm = hidden.shape
+    V = w_lm.shape[0]
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16, (M, Dm), dev)
+    _need(w_lm, "w_lm", torch.bfloat16, (V, Dm), dev)
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (M, V), dev)
+    _check(lib().isd_lm_head(_ptr(hidden), _ptr(w_lm), _ptr(out), M, Dm, V, _stream(dev)))
+    return out
+
+
+def lm_head_verify(hidden, w_lm, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
+                   with_diagnostics: bool = True, out: dict | None = None):
+    """The LM head and verification in one pass.  hidden [B (2N-1), Dm] bf16 (request-major),
+    w_lm [V, Dm] bf16, then verify()'s arguments.  Returns verify()'s dict plus
+    out["logits"] [B, 2N-1, V] bf16."""
+    B, R = uniforms.shape
+    if R % 2 == 0:
+        raise ValueError("uniforms must hold 2N-1 entries per request")
+    N = (R + 1) // 2
+    M, Dm = hidden.shape
+    V = w_lm.shape[0]
+    dev = hidden.device
+    if M != B * R:
+        raise ValueError(f"hidden has {M} rows, expected B (2N-1) = {B * R}")
+    _need(hidden, "hidden", torch.bfloat16, (M, Dm), dev)
+    _need(w_lm, "w_lm", torch.bfloat16, (V, Dm), dev)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.bfloat16, (B, N - 1, V), dev)
+    _need(draft_ids, "draft_ids", torch.int32, (B, N - 1), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, R), dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(logits=torch.empty((B, R, V), dtype=torch.bfloat16, device=dev),
+                   n_accept=torch.empty(B, **i32),
+                   accept=torch.empty((B, N - 1), dtype=torch.uint8, device=dev),
+                   next_token=torch.empty(B, **i32), argmax_ids=torch.empty((B, N), **i32),
+                   sampled_ids=torch.empty((B, N), **i32))
+        if with_diagnostics:
+            f32 = dict(dtype=torch.float32, device=dev)
+            out.update(p_draft=torch.empty((B, N - 1), **f32), q_draft=torch.empty((B, N - 1), **f32),
+                       row_lse=torch.empty((B, R + N - 1), **f32))
+    _need(out["logits"], "logits", torch.bfloat16, (B, R, V), dev)
+    L = lib()
+    nbytes = L.isd_lm_head_verify_workspace_bytes(B, N, V)
+    w = workspace("lm_head_verify", nbytes, dev, (B, N, V))
+    _check(L.isd_lm_head_verify(_ptr(hidden), _ptr(w_lm), _ptr(out["logits"]), _ptr(draft_logits),
+                                _ptr(draft_ids), _ptr(uniforms), B, N, Dm, V, float(temperature),
+                                _ptr(out["n_accept"]), _ptr(out["accept"]), _ptr(out["next_token"]),
+                                _ptr(out["argmax_ids"]), _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")),
+                                _ptr(out.get("q_draft")), _ptr(out.get("row_lse")), _ptr(w), w.numel(),
+                                _stream(dev)))
+    return out

@@ -337,13 +337,14 @@ def lm_head_inputs(cfg: LmHeadConfig, seed: int | None = None, argmax_drafts: bo
     B, N, R, V = cfg.B, cfg.N, cfg.R, cfg.V
     if cfg.grid:
         hidden = bf16_rne(_grid(g["x"], (cfg.M, cfg.Dm), 4, 0.25))
-        w_lm = bf16_rne(_grid(g["w"], (V, cfg.Dm), 2, 1.0 / 32.0))
     else:
         hidden = bf16_rne(normal(g["x"], (cfg.M, cfg.Dm), cfg.h_sd))
-        w_lm = np.empty((V, cfg.Dm), np.uint16)
-        step = 8192                                      # bounded float32 temporaries
-        for v0 in range(0, V, step):
-            w_lm[v0:v0 + step] = bf16_rne(normal(g["w"], (min(step, V - v0), cfg.Dm), cfg.w_sd))
+    w_lm = np.empty((V, cfg.Dm), np.uint16)
+    step = 8192                                          # bounded temporaries, in row order
+    for v0 in range(0, V, step):
+        shape = (min(step, V - v0), cfg.Dm)
+        rows = _grid(g["w"], shape, 2, 1.0 / 32.0) if cfg.grid else normal(g["w"], shape, cfg.w_sd)
+        w_lm[v0:v0 + step] = bf16_rne(rows)
     draft_stored = bf16_rne(normal(g["anchor"], (B, N - 1, V), cfg.draft_sd))
     draft_vals = bf16_bits_to_f32(draft_stored)
     if argmax_drafts:

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -179,3 +179,47 @@ def test_workspace_queries_grow_with_shape(L):
 def test_commit_validation(L, args, status):
     """Checked on the host before any launch (no GPU needed)."""
     assert L.isd_commit(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE, 448, 4096, 151936), INVALID),            # null hidden
+    ((FAKE, FAKE, None, 448, 4096, 151936), INVALID),            # null logits
+    ((FAKE, FAKE, FAKE, 0, 4096, 151936), INVALID),              # no rows
+    ((FAKE, FAKE, FAKE, 65537, 4096, 151936), INVALID),          # too many rows
+    ((FAKE, FAKE, FAKE, 448, 4080, 151936), UNSUPPORTED),        # Dm % 32
+    ((FAKE, FAKE, FAKE, 448, 4096, 151937), UNSUPPORTED),        # V % 8
+    ((FAKE, FAKE, FAKE, 448, 4096, (1 << 20) + 8), UNSUPPORTED), # V too large
+])
+def test_lm_head_validation(L, args, status):
+    assert L.isd_lm_head(*args, None) == status
+
+
+def lmv(L, **kw):
+    a = dict(B=64, N=4, Dm=4096, V=151936, T=1.0, h=FAKE, ids=FAKE, acc=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return L.isd_lm_head_verify(a["h"], FAKE, FAKE, FAKE, a["ids"], FAKE, a["B"], a["N"], a["Dm"],
+                                a["V"], ctypes.c_float(a["T"]), FAKE, a["acc"], FAKE, FAKE, FAKE,
+                                None, None, None, a["ws"], ctypes.c_size_t(a["wsb"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID),
+    (dict(N=9), UNSUPPORTED),
+    (dict(B=10000, N=4), INVALID),       # 70000 rows > 65536
+    (dict(h=None), INVALID),
+    (dict(Dm=100), UNSUPPORTED),
+    (dict(V=1001), UNSUPPORTED),
+    (dict(T=-1.0), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(acc=None), INVALID),
+    (dict(wsb=4096), WORKSPACE),
+    (dict(ws=None), WORKSPACE),
+])
+def test_lm_head_verify_validation(L, kw, status):
+    assert lmv(L, **kw) == status
+
+
+def test_lm_head_verify_workspace_holds_the_verification_records(L):
+    need = L.isd_lm_head_verify_workspace_bytes(64, 4, 151936)
+    assert need > L.isd_verify_workspace_bytes(64, 4, 151936) > 0
+    assert L.isd_lm_head_verify_workspace_bytes(0, 4, 151936) == 0
