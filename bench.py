@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="R-ISD decoder layer (Qwen3-8B shapes): gated against base-only time")
     ap.add_argument("--sweep-n", default="2,3,4")
+    ap.add_argument("--lm-head", action="store_true",
+                    help="the LM head fused with verification (Qwen3-8B shapes) against the unfused pair")
     return ap.parse_args()
 
 
@@ -94,6 +96,9 @@ def main():
         return
     if args.layer:
         layer_alpha(args)
+        return
+    if args.lm_head:
+        lm_head_bench(args)
         return
     import torch
 
@@ -543,6 +548,74 @@ def layer_alpha(args):
                       "base_only_us": round(res[False], 2), "gated_us": round(res[True], 2),
                       "alpha": round(res[True] / res[False], 4), "linears": per,
                       "timing": "hip graph replay of the layer; linears with events (warm weights)"}), flush=True)
+
+
+def lm_head_bench(args):
+    """The LM head in front of verification at Qwen3-8B's shapes: 64 requests x 7 rows,
+    hidden 4096, vocabulary 151936 (hidden ~ N(0,1), weights ~ N(0, 3/64), so logits have
+    sd ~3).  The previous step's proposal rows stand in as the verify rows' own logits plus
+    N(0, 0.3) noise, with drafts drawn from them by the Gumbel-max trick, so acceptance is
+    that of the verification workload.  Times, with events over --steps calls each: the LM
+    head alone, the LM head then verification, and the fused call."""
+    import torch
+
+    from strided_verify_propose_amd import isd, synth
+    cfg = synth.LM_HEAD_8B
+    B, N, R, Dm, V = cfg.B, cfg.N, cfg.R, cfg.Dm, cfg.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    h = torch.randn((cfg.M, Dm), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((V, Dm), generator=g, device=dev) * cfg.w_sd).to(torch.bfloat16)
+    logits = isd.lm_head(h, w).view(B, R, V)
+    draft = (logits[:, :N - 1].float() + 0.3 * torch.randn((B, N - 1, V), generator=g, device=dev))
+    gum = -torch.log(-torch.log(torch.rand(draft.shape, generator=g, device=dev).clamp_min(1e-30)))
+    ids = torch.argmax(draft + gum, dim=-1).to(torch.int32).contiguous()
+    draft = draft.to(torch.bfloat16).contiguous()
+    del gum
+    u = (torch.randint(0, 1 << 24, (B, R), generator=g, device=dev).float() / float(1 << 24)).contiguous()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    out_l = torch.empty((cfg.M, V), dtype=torch.bfloat16, device=dev)
+    t_head = timed(lambda: isd.lm_head(h, w, out=out_l))
+    vout = {}
+
+    def unfused():
+        isd.lm_head(h, w, out=out_l)
+        vout["r"] = isd.verify(out_l.view(B, R, V), draft, ids, u, with_diagnostics=False,
+                               out=vout.get("r"))
+    t_unfused = timed(unfused)
+    fout = {}
+
+    def fused():
+        fout["r"] = isd.lm_head_verify(h, w, draft, ids, u, with_diagnostics=False, out=fout.get("r"))
+    t_fused = timed(fused)
+    n_acc = fout["r"]["n_accept"].float().mean().item()
+    flops = 2.0 * cfg.M * Dm * V
+    w_bytes = V * Dm * 2
+    print(json.dumps({
+        "lm_head": "qwen3_8b_b64_n4", "rows": cfg.M, "hidden": Dm, "vocab": V, "data": "synthetic",
+        "steps": args.steps, "lm_head_us": round(t_head, 2), "lm_head_then_verify_us": round(t_unfused, 2),
+        "fused_us": round(t_fused, 2), "fusion_saving_us": round(t_unfused - t_fused, 2),
+        "lm_head_tflops": round(flops / (t_head * 1e-6) / 1e12, 1),
+        "lm_head_mfma_frac": round(flops / (t_head * 1e-6) / 2.5e15, 4),
+        "lm_head_weight_GBps": round(w_bytes / (t_head * 1e-6) / 1e9, 1),
+        "mean_n_accept": round(n_acc, 3),
+        "timing": "events around --steps back-to-back calls (weights 1.24 GB, streamed from HBM each call)"}),
+        flush=True)
 
 
 def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):

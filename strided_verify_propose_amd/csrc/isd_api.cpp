@@ -88,7 +88,7 @@ LmhWs lmh_ws(int B, int N, int V) {
   LmhWs w{};
   w.v = ver_ws(B, N, V);
   w.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
-  const size_t recs = (size_t)B * (2 * N - 1) * w.NMINI;
+  const size_t recs = (size_t)B * (2 * N - 1) * ((w.NMINI + 7) & ~7);
   w.mmax = w.v.total;
   w.msum = w.mmax + align256(recs * sizeof(float));
   w.marg = w.msum + align256(recs * sizeof(float));
@@ -137,6 +137,7 @@ isd::LmhLaunch lmh_launch(const void* hidden, const void* w_lm, void* logits, in
   p.logits = static_cast<uint16_t*>(logits);
   p.M = M; p.Dm = Dm; p.V = V;
   p.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
+  p.NMS = (p.NMINI + 7) & ~7;
   p.c2 = c2;
   return p;
 }

@@ -84,10 +84,11 @@ struct LmhLaunch {
   const uint16_t* w;            // [V, Dm] bf16
   uint16_t* logits;             // [M, V] bf16 out
   int M, Dm, V, NMINI;          // NMINI = ceil(V / LMH_BN)
+  int NMS;                      // row stride of the mini-chunk records: NMINI rounded up to 8
   float c2;                     // log2(e)/T
-  float* mmax;                  // [M][NMINI] mini-chunk max; null: logits only
-  float* msum;                  // [M][NMINI] sum 2^(l c2 - fp32(max c2))
-  int32_t* marg;                // [M][NMINI] lowest column holding the max
+  float* mmax;                  // [M][NMS] mini-chunk max; null: logits only
+  float* msum;                  // [M][NMS] sum 2^(l c2 - fp32(max c2))
+  int32_t* marg;                // [M][NMS] lowest column holding the max
   // merge into the verification's records (rows b RR + r, r < R)
   int N, R, RR, SV, NSUB;
   float* cmax;

@@ -10,16 +10,21 @@
 //              (4 x 112) x (2 x 64) over 8 waves, two per SIMD, each wave 7 x 4 blocks of
 //              v_mfma_f32_16x16x32_bf16.  Both operands are K-contiguous (hidden rows, w_lm
 //              rows), so a k step of 32 is 36 MFMA fragments of 16 rows x 64 bytes (28 of
-//              hidden, 8 of w_lm), which the waves load straight into LDS in fragment order
-//              (global_load_lds_dwordx4: lane l's 16 bytes land at slot l, which is lane
-//              l's MFMA operand, so the operand reads are conflict-free).  A ring of RING
-//              such slots keeps RING - 1 steps of loads in flight; one barrier per step.
+//              hidden, 8 of w_lm), which the waves load straight into LDS
+//              (global_load_lds_dwordx4: lane l's 16 bytes land at slot l).  For coalescing,
+//              four consecutive lanes read one row's 64 contiguous bytes: lane l takes row
+//              l / 4 of the fragment and 16-byte chunk (l % 4) ^ (row / 4), so chunk c of
+//              row r sits at slot 4 r + (c ^ (r / 4)), where the MFMA lane holding
+//              (r, c) reads it -- the xor keeps every 16-lane read on distinct banks.  A
+//              ring of RING slots keeps RING - 1 steps of loads in flight; one barrier per
+//              step, after which the waves read the next step's fragments while the current
+//              step's MFMAs run.
 //              The epilogue rounds the tile to bf16 (nearest even), passes it through LDS so
 //              that every lane stores 32 contiguous bytes of a row, and -- when statistics are
 //              asked for -- reduces each row's 128 values to a mini-chunk record: the max m of
 //              the stored values, the lowest column holding it, and the sum of
 //              2^(l c2 - K) with K = fp32(m c2).
-// lmh_merge_kernel  One wave per row: mini-chunk records -> the verification's chunk
+// lmh_merge_kernel  One wave per row and 64 sub-chunks: mini-chunk records -> the verification's chunk
 //              records (16384 columns: max, lowest argmax, K = fp32(max c2)) and sub-chunk
 //              sums (1024 columns) against the chunk's K, rescaled and added in fp64 in
 //              column order.  The walk, residual and draw kernels then run unchanged.
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int wm = wave >> 1, wn = wave & 1;
-  const int l16 = lane & 15, kq = 8 * (lane >> 4);
+  const int l16 = lane & 15;
   const int m0 = tm * LMH_BM, n0 = tn * BN;
   const int S = p.Dm / 32;
 
@@ -79,14 +84,16 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
 
   // This wave's fragment loads: fragment f = wave + 8 i (i < LPW, f < NF); f < AF is
   // hidden row block f, else w_lm block f - AF.  Rows past M read row M-1 and columns
-  // past V read row V-1 of w_lm (in bounds; never stored).
+  // past V read row V-1 of w_lm (in bounds; never stored).  Lane l loads row l / 4 of the
+  // fragment, chunk (l % 4) ^ (row / 4).
   const uint16_t* src[LPW];
   int dst[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int f = min(wave + WAVES * i, NF - 1);
-    src[i] = f < AF ? p.hidden + (size_t)min(m0 + 16 * f + l16, p.M - 1) * p.Dm + kq
-                    : p.w + (size_t)min(n0 + 16 * (f - AF) + l16, p.V - 1) * p.Dm + kq;
+    const int fr_row = lane >> 2, fr_chunk = (lane & 3) ^ (fr_row >> 2);
+    src[i] = f < AF ? p.hidden + (size_t)min(m0 + 16 * f + fr_row, p.M - 1) * p.Dm + 8 * fr_chunk
+                    : p.w + (size_t)min(n0 + 16 * (f - AF) + fr_row, p.V - 1) * p.Dm + 8 * fr_chunk;
     dst[i] = f * 1024;
   }
   const bool extra = wave < NF - (LPW - 1) * WAVES;  // this wave has an LPW-th fragment
@@ -104,29 +111,46 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Step s: wait until this wave's loads of step s have landed (steps s + 1 .. s + RING - 2
-  // may still be in flight), barrier (every wave's step-s fragments are in, and every wave
-  // is done with step s - 1's slot), then load step s + RING - 1 into that slot and run
-  // step s from LDS.
+  // Fragments of step s + 1 are read from LDS while step s's MFMAs run: at step s the
+  // wait covers step s + 1's loads, and the barrier then makes them visible.
+  struct Frag { u32x4 a[RB], b[CB]; };
+  auto read = [&](Frag& F, int step) {
+    const u32x4* fr = reinterpret_cast<const u32x4*>(smem + (step % RING) * SLOT);
+    const int rd = 4 * l16 + ((lane >> 4) ^ (l16 >> 2));
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) issue(u);
-  for (int s = 0; s < S; ++s) {
-    if (extra) wait_vmcnt<(RING - 2) * LPW>();
-    else wait_vmcnt<(RING - 2) * (LPW - 1)>();
+    for (int j = 0; j < CB; ++j) F.b[j] = fr[(AF + CB * wn + j) * 64 + rd];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) F.a[i] = fr[(RB * wm + i) * 64 + rd];
+  };
+  auto sync_next = [&]() {
+    if (extra) wait_vmcnt<LPW>();
+    else wait_vmcnt<LPW - 1>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  auto body = [&](int s, const Frag& cur, Frag& nxt) {
+    sync_next();
     issue(s + RING - 1);
-    const u32x4* fr = reinterpret_cast<const u32x4*>(smem + (s % RING) * SLOT);
-    u32x4 a[RB], b[CB];
-#pragma unroll
-    for (int j = 0; j < CB; ++j) b[j] = fr[(AF + CB * wn + j) * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) a[i] = fr[(RB * wm + i) * 64 + lane];
+    read(nxt, s + 1);
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
-      for (int j = 0; j < CB; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < CB; ++j) acc[i][j] = mfma16x16x32(cur.a[i], cur.b[j], acc[i][j]);
+  };
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) issue(u);
+  Frag F0, F1;
+  if (extra) wait_vmcnt<LPW>();
+  else wait_vmcnt<LPW - 1>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  read(F0, 0);
+  int s = 0;
+  for (; s + 2 <= S; s += 2) {
+    body(s, F0, F1);
+    body(s + 1, F1, F0);
   }
+  if (s < S) body(s, F0, F1);
   wait_vmcnt<0>();
   __syncthreads();  // the ring is dead: reuse it as the output tile
 
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
     sum += __shfl_xor(sum, 2);
     sum += __shfl_xor(sum, 4);
     if (q == 0 && row < p.M) {
-      const size_t o = (size_t)row * p.NMINI + tn;
+      const size_t o = (size_t)row * p.NMS + tn;
       p.mmax[o] = m;
       p.msum[o] = sum;
       p.marg[o] = arg;
@@ -201,9 +225,10 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
   }
 }
 
-// One wave per logits row m = b R + rr (rr < R): mini-chunk records -> chunk records and
-// sub-chunk sums at verification row b RR + rr.  Lane l of round t takes sub-chunk
-// 64 t + l; the 16 lanes of a 16-lane group are the 16 sub-chunks of one chunk.
+// Wave (row m = b R + rr, round t): mini-chunk records -> chunk records and sub-chunk sums
+// at verification row b RR + rr, for sub-chunks 64 t .. 64 t + 63.  Lane l takes
+// sub-chunk 64 t + l (its 8 records are 32 aligned bytes per array); the 16 lanes of a
+// 16-lane group are the 16 sub-chunks of one chunk.
 __global__ __launch_bounds__(256) void lmh_merge_kernel(const LmhLaunch p) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -212,52 +237,61 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(const LmhLaunch p) {
   const size_t rowid = (size_t)b * p.RR + rr;
   const bool proposal = rr >= p.N - 1;
   const float c2 = p.c2;
-  const float* mm = p.mmax + (size_t)m * p.NMINI;
-  const float* ms = p.msum + (size_t)m * p.NMINI;
-  const int32_t* ma = p.marg + (size_t)m * p.NMINI;
   constexpr int MPS = VSUB / BN;  // mini-chunks per sub-chunk
-  for (int j0 = 0; j0 < p.NSUB; j0 += 64) {
-    const int j = j0 + lane;
-    const bool valid = j < p.NSUB;
-    float mt[MPS], stt[MPS];
-    int at[MPS];
+  static_assert(MPS == 8, "two 16-byte loads per array and lane");
+  const int j = 64 * blockIdx.y + lane;
+  const bool valid = j < p.NSUB;
+  const int jc = valid ? j : 0;
+  const size_t o = (size_t)m * p.NMS + (size_t)MPS * jc;  // 32-byte aligned (NMS % 8 == 0)
+  float mt[MPS], stt[MPS];
+  int at[MPS];
 #pragma unroll
-    for (int t = 0; t < MPS; ++t) {
-      const int idx = j * MPS + t;
-      const bool ok = valid && idx < p.NMINI;
-      const int ci = ok ? idx : 0;
-      mt[t] = ok ? mm[ci] : -__builtin_inff();
-      stt[t] = ok ? ms[ci] : 0.f;
-      at[t] = ok ? ma[ci] : INT_MAX;
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p.mmax + o + 4 * h);
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(p.msum + o + 4 * h);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(p.marg + o + 4 * h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mt[4 * h + e] = a[e];
+      stt[4 * h + e] = b4[e];
+      at[4 * h + e] = (int)c[e];
     }
-    float sm = -__builtin_inff();
-    int sa = INT_MAX;
+  }
+  // records past the row's last mini-chunk are padding (never written): masked here
 #pragma unroll
-    for (int t = 0; t < MPS; ++t)
-      if (mt[t] > sm) {  // strictly greater: ties keep the lower column
-        sm = mt[t];
-        sa = at[t];
-      }
-    float M = sm;
+  for (int t = 0; t < MPS; ++t)
+    if (!valid || MPS * j + t >= p.NMINI) {
+      mt[t] = -__builtin_inff();
+      stt[t] = 0.f;
+      at[t] = INT_MAX;
+    }
+  float sm = -__builtin_inff();
+  int sa = INT_MAX;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    int A = (sm == M) ? sa : INT_MAX;
+  for (int t = 0; t < MPS; ++t)
+    if (mt[t] > sm) {  // strictly greater: ties keep the lower column
+      sm = mt[t];
+      sa = at[t];
+    }
+  float M = sm;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) A = min(A, __shfl_xor(A, o));
-    const float Kc = __fmul_rn(M, c2);
-    double acc = 0.0;
+  for (int d = 8; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+  int A = (sm == M) ? sa : INT_MAX;
 #pragma unroll
-    for (int t = 0; t < MPS; ++t)
-      if (mt[t] > -__builtin_inff())
-        acc += (double)stt[t] * exp2((double)__fmul_rn(mt[t], c2) - (double)Kc);
-    if (valid) {
-      p.csub[rowid * p.NSUB + j] = (float)acc;
-      if ((lane & 15) == 0) {
-        const int c = j / VCHUNK_SUBS;
-        p.cmax[rowid * p.SV + c] = M;
-        p.cref[rowid * p.SV + c] = Kc;
-        p.cidx[rowid * p.SV + c] = proposal ? A : INT_MAX;
-      }
+  for (int d = 8; d >= 1; d >>= 1) A = min(A, __shfl_xor(A, d));
+  const float Kc = __fmul_rn(M, c2);
+  double acc = 0.0;
+#pragma unroll
+  for (int t = 0; t < MPS; ++t)
+    if (mt[t] > -__builtin_inff())
+      acc += (double)stt[t] * exp2((double)__fmul_rn(mt[t], c2) - (double)Kc);
+  if (valid) {
+    p.csub[rowid * p.NSUB + j] = (float)acc;
+    if ((lane & 15) == 0) {
+      const int c = j / VCHUNK_SUBS;
+      p.cmax[rowid * p.SV + c] = M;
+      p.cref[rowid * p.SV + c] = Kc;
+      p.cidx[rowid * p.SV + c] = proposal ? A : INT_MAX;
     }
   }
 }
@@ -271,7 +305,7 @@ hipError_t launch_lm_head(const LmhLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_lm_head_merge(const LmhLaunch& p, hipStream_t s) {
-  lmh_merge_kernel<<<(p.M + 3) / 4, 256, 0, s>>>(p);
+  lmh_merge_kernel<<<dim3((p.M + 3) / 4, (p.NSUB + 63) / 64), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
