@@ -69,7 +69,11 @@ def test_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         print(f"  replay {rep}: eager junk n_accept sum {int(junk['n_accept'].sum())}", flush=True)
-        assert torch.equal(y, ref["y"]), f"projection differs on replay {rep}"
+        if not torch.equal(y, ref["y"]):
+            d = (y != ref["y"]).cpu().numpy()
+            raise AssertionError(f"projection differs on replay {rep}: {int(d.sum())} elements in rows "
+                                 f"{np.flatnonzero(d.any(1)).tolist()[:16]}, columns "
+                                 f"{np.flatnonzero(d.any(0)).tolist()[:16]}")
         assert torch.equal(att_out, ref["att"]), f"attention differs on replay {rep}"
         assert torch.equal(A["k_cache"], ref["k"]) and torch.equal(A["v_cache"], ref["v"]), "cache"
         for k, t in vout.items():
