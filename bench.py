@@ -603,6 +603,8 @@ def lm_head_bench(args):
     def fused():
         fout["r"] = isd.lm_head_verify(h, w, draft, ids, u, with_diagnostics=False, out=fout.get("r"))
     t_fused = timed(fused)
+    # reference only: the vendor GEMM (hipBLASLt through torch) on the same product
+    t_lib = timed(lambda: torch.nn.functional.linear(h, w))
     n_acc = fout["r"]["n_accept"].float().mean().item()
     flops = 2.0 * cfg.M * Dm * V
     w_bytes = V * Dm * 2
@@ -613,6 +615,7 @@ def lm_head_bench(args):
         "lm_head_tflops": round(flops / (t_head * 1e-6) / 1e12, 1),
         "lm_head_mfma_frac": round(flops / (t_head * 1e-6) / 2.5e15, 4),
         "lm_head_weight_GBps": round(w_bytes / (t_head * 1e-6) / 1e9, 1),
+        "reference_torch_linear_us": round(t_lib, 2),
         "mean_n_accept": round(n_acc, 3),
         "timing": "events around --steps back-to-back calls (weights 1.24 GB, streamed from HBM each call)"}),
         flush=True)

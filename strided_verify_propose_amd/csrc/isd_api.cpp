@@ -87,7 +87,7 @@ struct LmhWs {
 LmhWs lmh_ws(int B, int N, int V) {
   LmhWs w{};
   w.v = ver_ws(B, N, V);
-  w.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
+  w.NMINI = (V + isd::LMH_MINI - 1) / isd::LMH_MINI;
   const size_t recs = (size_t)B * (2 * N - 1) * ((w.NMINI + 7) & ~7);
   w.mmax = w.v.total;
   w.msum = w.mmax + align256(recs * sizeof(float));
@@ -136,7 +136,7 @@ isd::LmhLaunch lmh_launch(const void* hidden, const void* w_lm, void* logits, in
   p.w = static_cast<const uint16_t*>(w_lm);
   p.logits = static_cast<uint16_t*>(logits);
   p.M = M; p.Dm = Dm; p.V = V;
-  p.NMINI = (V + isd::LMH_BN - 1) / isd::LMH_BN;
+  p.NMINI = (V + isd::LMH_MINI - 1) / isd::LMH_MINI;
   p.NMS = (p.NMINI + 7) & ~7;
   p.c2 = c2;
   return p;

@@ -76,14 +76,13 @@ hipError_t launch_verify_stats(const VerifyLaunch& v, hipStream_t s);  // the st
 hipError_t launch_verify_tail(const VerifyLaunch& v, hipStream_t s);   // walk, residual, draws
 
 // ---------------------------------------------------------------- LM head
-constexpr int LMH_BM = 448;     // rows per LM-head workgroup (4 waves of 112)
-constexpr int LMH_BN = 128;     // vocabulary columns per LM-head workgroup (one mini-chunk)
+constexpr int LMH_MINI = 128;   // vocabulary columns per mini-chunk record of the LM head
 
 struct LmhLaunch {
   const uint16_t* hidden;       // [M, Dm] bf16, row b R + r
   const uint16_t* w;            // [V, Dm] bf16
   uint16_t* logits;             // [M, V] bf16 out
-  int M, Dm, V, NMINI;          // NMINI = ceil(V / LMH_BN)
+  int M, Dm, V, NMINI;          // NMINI = ceil(V / LMH_MINI)
   int NMS;                      // row stride of the mini-chunk records: NMINI rounded up to 8
   float c2;                     // log2(e)/T
   float* mmax;                  // [M][NMS] mini-chunk max; null: logits only

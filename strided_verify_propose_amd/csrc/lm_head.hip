@@ -6,11 +6,11 @@
 // 「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD"); the vocabulary
 // projection that produces those rows is this product.
 //
-// lmh_kernel   One workgroup per 448-row x 128-column tile; wave w owns rows
-//              (4 x 112) x (2 x 64) over 8 waves, two per SIMD, each wave 7 x 4 blocks of
-//              v_mfma_f32_16x16x32_bf16.  Both operands are K-contiguous (hidden rows, w_lm
-//              rows), so a k step of 32 is 36 MFMA fragments of 16 rows x 64 bytes (28 of
-//              hidden, 8 of w_lm), which the waves load straight into LDS
+// lmh_kernel   One workgroup per 224-row x 256-column tile, (2 x 112) x (4 x 64) over 8
+//              waves, two per SIMD, each wave 7 x 4 blocks of v_mfma_f32_16x16x32_bf16.
+//              Both operands are K-contiguous (hidden rows, w_lm rows), so a k step of 32
+//              is 30 MFMA fragments of 16 rows x 64 bytes (14 of hidden, 16 of w_lm), which
+//              the waves load straight into LDS
 //              (global_load_lds_dwordx4: lane l's 16 bytes land at slot l).  For coalescing,
 //              four consecutive lanes read one row's 64 contiguous bytes: lane l takes row
 //              l / 4 of the fragment and 16-byte chunk (l % 4) ^ (row / 4), so chunk c of
@@ -39,22 +39,23 @@ namespace {
 
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
-constexpr int WM = LMH_BM / 4;      // 112 rows per wave (waves 4 in M x 2 in N)
-constexpr int WN = LMH_BN / 2;      // 64 columns per wave
-constexpr int BN = LMH_BN;          // 128 columns per workgroup
+constexpr int TBM = 224;            // rows per workgroup
+constexpr int TBN = 256;            // columns per workgroup
+constexpr int WM = TBM / 2;         // 112 rows per wave (waves 2 in M x 4 in N)
+constexpr int WN = TBN / 4;         // 64 columns per wave
+constexpr int BN = LMH_MINI;        // 128 columns per mini-chunk record
 constexpr int RB = WM / 16;         // 7 row blocks per wave
 constexpr int CB = WN / 16;         // 4 column blocks per wave
-constexpr int AF = LMH_BM / 16;     // 28 hidden fragments per k step
-constexpr int BF = BN / 16;         // 8 w_lm fragments per k step
-constexpr int NF = AF + BF;         // 36 fragments (1 KB each) per k step
-constexpr int LPW = (NF + WAVES - 1) / WAVES;  // loads per wave per step: 5 (waves 0..3), 4 (4..7)
+constexpr int AF = TBM / 16;        // 14 hidden fragments per k step
+constexpr int BF = TBN / 16;        // 16 w_lm fragments per k step
+constexpr int NF = AF + BF;         // 30 fragments (1 KB each) per k step
+constexpr int LPW = (NF + WAVES - 1) / WAVES;  // loads per wave per step: 4 (waves 0..5), 3 (6..7)
 constexpr int RING = 4;             // LDS slots: RING - 1 k steps of loads in flight
 constexpr int SLOT = NF * 1024;     // bytes per slot
-constexpr int LROW = BN + 8;        // LDS row stride of the epilogue tile, in bf16
-static_assert(LMH_BM % 64 == 0 && BN == 128, "tile shape");
-static_assert(NF - (LPW - 1) * WAVES == WAVES / 2, "waves 0..3 take one more fragment than 4..7");
+constexpr int LROW = TBN + 8;       // LDS row stride of the epilogue tile, in bf16
+static_assert(BN == 128 && TBN == 2 * BN && TBM % 16 == 0, "tile shape: two mini-chunks per row");
 static_assert(VCHUNK % BN == 0 && VSUB % BN == 0, "mini-chunks tile the chunks");
-static_assert((size_t)LMH_BM * LROW * 2 <= (size_t)RING * SLOT, "the epilogue tile fits in the ring");
+static_assert((size_t)TBM * LROW * 2 <= (size_t)RING * SLOT, "the epilogue tile fits in the ring");
 
 // s_waitcnt with only the vector-memory count bounded (gfx9 encoding: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -69,14 +70,14 @@ __device__ __forceinline__ void load_frag(const uint16_t* src, unsigned char* ld
 }
 
 __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
-  const int mt = (p.M + LMH_BM - 1) / LMH_BM, nt = p.NMINI;
+  const int mt = (p.M + TBM - 1) / TBM, nt = (p.NMINI + 1) / 2;
   int tm, tn;
   if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15;
-  const int m0 = tm * LMH_BM, n0 = tn * BN;
+  const int m0 = tm * TBM, n0 = tn * TBN;
   const int S = p.Dm / 32;
 
   // LDS: RING slots of NF fragments during the K loop, then the bf16 output tile.
@@ -166,14 +167,16 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
             (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
   __syncthreads();
 
-  // wave w: tile rows 56 w .. 56 w + 55, eight lanes per row (16 columns each)
-  constexpr int RPW = LMH_BM / WAVES;
-  const int q = lane & 7;
+  // wave w: tile rows 28 w .. 28 w + 27, sixteen lanes per row (16 columns each); lanes
+  // 0..7 and 8..15 of a row are its two mini-chunks
+  constexpr int RPW = TBM / WAVES;
+  const int q = lane & 15;
   const float c2 = p.c2;
-  for (int pass = 0; pass < RPW / 8; ++pass) {
-    const int rl = RPW * wave + 8 * pass + (lane >> 3);
+  for (int pass = 0; pass < RPW / 4; ++pass) {
+    const int rl = RPW * wave + 4 * pass + (lane >> 4);
     const int row = m0 + rl;
     const int cbase = n0 + 16 * q;
+    const int mini = 2 * tn + (q >> 3);
     u32x4 w2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) w2[h] = *reinterpret_cast<const u32x4*>(&t[rl][16 * q + 8 * h]);
@@ -216,8 +219,8 @@ __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
     sum += __shfl_xor(sum, 1);
     sum += __shfl_xor(sum, 2);
     sum += __shfl_xor(sum, 4);
-    if (q == 0 && row < p.M) {
-      const size_t o = (size_t)row * p.NMS + tn;
+    if ((q & 7) == 0 && row < p.M && mini < p.NMINI) {
+      const size_t o = (size_t)row * p.NMS + mini;
       p.mmax[o] = m;
       p.msum[o] = sum;
       p.marg[o] = arg;
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(const LmhLaunch p) {
 }  // namespace
 
 hipError_t launch_lm_head(const LmhLaunch& p, hipStream_t s) {
-  const int mt = (p.M + LMH_BM - 1) / LMH_BM;
-  lmh_kernel<<<tile_grid(mt, p.NMINI), THREADS, 0, s>>>(p);
+  const int mt = (p.M + TBM - 1) / TBM;
+  lmh_kernel<<<tile_grid(mt, (p.NMINI + 1) / 2), THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
