@@ -84,7 +84,7 @@ def verify_bytes(B, N, V, n_rejected_sampled, s=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               f"(requests shard by data parallelism with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
