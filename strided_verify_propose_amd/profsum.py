@@ -6,8 +6,9 @@
 
 The HBM summary scales each kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a 1 GiB device-to-device copy in the same run, and
-records the SHA-256 of the attention sources it was taken on, so that a reader can
-tell when the counters no longer describe the kernel.
+records the SHA-256 of the attention sources it was taken on (attention.hip, device.h and
+the attention section of launch.h), so that a reader can tell when the counters no longer
+describe the kernel.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = ["csrc/attention.hip", "csrc/device.h", "csrc/launch.h"]
+# in launch.h only the attention section (up to the next section rule) feeds the kernel
+SECTION_OF = {"csrc/launch.h": "// ---------------------------------------------------------------- attention"}
+SECTION_RULE = "// ----------------------------------------------------------------"
 COPY_BYTES = 1 << 30
 
 
@@ -28,10 +32,16 @@ def attention_source_hash() -> str:
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
-            for line in fh:
-                code = line.split("//", 1)[0].rstrip()
-                if code:
-                    h.update(code.encode() + b"\n")
+            lines = fh.read().splitlines()
+        if f in SECTION_OF:
+            start = lines.index(SECTION_OF[f])
+            end = next((i for i in range(start + 1, len(lines)) if lines[i].startswith(SECTION_RULE)),
+                       len(lines))
+            lines = lines[start:end]
+        for line in lines:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
