@@ -142,6 +142,7 @@ __device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int l
   put(lds[1], r[1], tid);
   lds_barrier();
   fetch_frags(f[0], lds[0], lane);
+  lds_barrier();  // every wave has read buffer 0 before step 0 refills it with step 2
   // Steps past the end re-load and re-stage the last step (unconditional loads keep the
   // compiler's wait counts exact); only the MFMAs are skipped.
   for (int s0 = 0; s0 < S; s0 += RING) {

@@ -74,3 +74,23 @@ def test_packed_layout():
 
     want = np.concatenate([frag_order(np.concatenate([w, a])), b.ravel()])
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("M", [56, 448])
+def test_back_to_back_calls_are_identical(M):
+    """Many calls in a row without synchronising, split-K (56 rows) and not (448 rows), on
+    both weight layouts: every result bitwise equal to the first.  Covers the order of the
+    first LDS refill against the waves' first fragment reads."""
+    cfg = synth.ProjConfig("b2b", B=8, N=4, K=4096, Nout=4096, r=128, x_sd=1.0, w_sd=0.02, seed=2030)
+    p = synth.proj_inputs(cfg, M=M)
+    x, w, a, b, g = (to_dev(t) for t in (p.x, p.w, p.a, p.b, p.gate))
+    packed = isd.pack_proj_weights(w, a, b)
+    print(f"back-to-back projection M={M} ksplit path={'yes' if M < 64 else 'no'}", flush=True)
+    for call in (lambda o: isd.gated_lora_proj(x, w, a, b, g, out=o),
+                 lambda o: isd.gated_lora_proj_packed(x, packed, g, out=o)):
+        outs = [torch.empty((M, cfg.Nout), dtype=torch.bfloat16, device="cuda") for _ in range(40)]
+        for o in outs:
+            call(o)
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs[1:], 1):
+            assert torch.equal(o, outs[0]), f"call {i} differs from call 0"
