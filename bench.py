@@ -553,14 +553,15 @@ def layer_alpha(args):
 def lm_head_bench(args):
     """The LM head in front of verification at Qwen3-8B's shapes: 64 requests x 7 rows,
     hidden 4096, vocabulary 151936 (hidden ~ N(0,1), weights ~ N(0, 3/64), so logits have
-    sd ~3).  The previous step's proposal rows stand in as the verify rows' own logits plus
-    N(0, 0.3) noise, with drafts drawn from them by the Gumbel-max trick, so acceptance is
-    that of the verification workload.  Times, with events over --steps calls each: the LM
-    head alone, the LM head then verification, and the fused call."""
+    sd ~3); --workload qwen3_32b takes hidden 5120.  The previous step's proposal rows
+    stand in as the verify rows' own logits plus N(0, 0.3) noise, with drafts drawn from
+    them by the Gumbel-max trick, so acceptance is that of the verification workload.
+    Times, with events over --steps calls each: the LM head alone, the LM head then
+    verification, and the fused call."""
     import torch
 
     from strided_verify_propose_amd import isd, synth
-    cfg = synth.LM_HEAD_8B
+    cfg = synth.LM_HEAD_32B if args.workload == "qwen3_32b" else synth.LM_HEAD_8B
     B, N, R, Dm, V = cfg.B, cfg.N, cfg.R, cfg.Dm, cfg.V
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -609,7 +610,7 @@ def lm_head_bench(args):
     flops = 2.0 * cfg.M * Dm * V
     w_bytes = V * Dm * 2
     print(json.dumps({
-        "lm_head": "qwen3_8b_b64_n4", "rows": cfg.M, "hidden": Dm, "vocab": V, "data": "synthetic",
+        "lm_head": cfg.name, "rows": cfg.M, "hidden": Dm, "vocab": V, "data": "synthetic",
         "steps": args.steps, "lm_head_us": round(t_head, 2), "lm_head_then_verify_us": round(t_unfused, 2),
         "fused_us": round(t_fused, 2), "fusion_saving_us": round(t_unfused - t_fused, 2),
         "lm_head_tflops": round(flops / (t_head * 1e-6) / 1e12, 1),
@@ -617,7 +618,8 @@ def lm_head_bench(args):
         "lm_head_weight_GBps": round(w_bytes / (t_head * 1e-6) / 1e9, 1),
         "reference_torch_linear_us": round(t_lib, 2),
         "mean_n_accept": round(n_acc, 3),
-        "timing": "events around --steps back-to-back calls (weights 1.24 GB, streamed from HBM each call)"}),
+        "timing": f"events around --steps back-to-back calls (weights {w_bytes / 1e9:.2f} GB, streamed "
+                  f"from HBM each call)"}),
         flush=True)
 
 

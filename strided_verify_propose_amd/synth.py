@@ -310,10 +310,12 @@ class LmHeadConfig:
         return self.B * self.R
 
 
-# Qwen3-8B's hidden size and vocabulary; weights scaled so the logits have sd ~3 like the
-# verification workload's anchors.
+# Qwen3-8B's and Qwen3-32B's hidden sizes and vocabulary; weights scaled so the logits
+# have sd ~3 like the verification workload's anchors.
 LM_HEAD_8B = LmHeadConfig("lm_head_qwen3_8b_b64_n4", B=64, N=4, Dm=4096, V=151936,
                           h_sd=1.0, w_sd=3.0 / 64.0, draft_sd=3.0, grid=False, seed=1005)
+LM_HEAD_32B = LmHeadConfig("lm_head_qwen3_32b_b64_n4", B=64, N=4, Dm=5120, V=151936,
+                           h_sd=1.0, w_sd=3.0 / 5120 ** 0.5, draft_sd=3.0, grid=False, seed=1006)
 
 
 @dataclass

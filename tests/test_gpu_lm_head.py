@@ -162,3 +162,24 @@ def test_lm_head_verify_deterministic():
     b = isd.lm_head_verify(*args)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_lm_head_qwen3_32b_hidden_sampled_rows():
+    """Hidden size 5120 (Qwen3-32B) on the exact grid: sampled rows bit for bit."""
+    c = lcfg("qwen3_32b_grid", 64, 4, 5120, 151936, 62)
+    x = synth.lm_head_inputs(c)
+    out = to_np(isd.lm_head(to_dev(x.hidden), to_dev(x.w_lm)))
+    rows = [0, 1, 223, 224, 300, 447]
+    assert np.array_equal(as_f64(out[rows]), oracle_logits(x.hidden, x.w_lm, rows))
+
+
+def test_lm_head_verify_back_to_back_calls_are_identical():
+    c = lcfg("b2b", 16, 4, 1024, 40000, 63, grid=False)
+    x = synth.lm_head_inputs(c)
+    args = (to_dev(x.hidden), to_dev(x.w_lm), to_dev(x.draft_logits), to_dev(x.draft_ids),
+            to_dev(x.uniforms))
+    outs = [isd.lm_head_verify(*args) for _ in range(12)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for k in o:
+            assert torch.equal(o[k], outs[0][k]), k
