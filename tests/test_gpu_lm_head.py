@@ -35,6 +35,7 @@ LOGIT_CASES = [
     lcfg("m448_dm4096_v2048", 64, 4, 4096, 2048, 42),
     lcfg("m700_dm96_v1032", 100, 4, 96, 1032, 43),   # two row tiles, the second ragged; 3 k steps
     lcfg("m9_dm160_v4104", 3, 2, 160, 4104, 44),
+    lcfg("m1_dm64_v1000", 1, 1, 64, 1000, 46),      # a single row; two k steps, fewer than the ring
 ]
 
 
