@@ -606,6 +606,13 @@ def lm_head_bench(args):
     t_fused = timed(fused)
     # reference only: the vendor GEMM (hipBLASLt through torch) on the same product
     t_lib = timed(lambda: torch.nn.functional.linear(h, w))
+    if args.copy_calibration:  # a 1 GiB device copy for the HBM counters' scale
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     n_acc = fout["r"]["n_accept"].float().mean().item()
     flops = 2.0 * cfg.M * Dm * V
     w_bytes = V * Dm * 2

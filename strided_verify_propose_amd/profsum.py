@@ -64,19 +64,19 @@ def trace(stats_csv, out, command):
 
 
 def per_kernel(counter_csv, counter):
-    """{kernel name: [value per dispatch]} and the value of the last copy dispatch (the
-    benchmark ends with its 1 GiB calibration copies)."""
+    """{kernel name: [value per dispatch]} and the largest value of the runtime's
+    buffer-copy kernel: the benchmark's 1 GiB calibration copy (a same-dtype device copy),
+    far larger than the small copies around it.  Dtype conversions run other kernels."""
     vals = defaultdict(list)
-    last_copy = (-1, 0.0)
+    big_copy = 0.0
     for r in csv.DictReader(open(counter_csv)):
         if r["Counter_Name"] != counter:
             continue
         v = float(r["Counter_Value"])
         vals[r["Kernel_Name"]].append(v)
-        d = int(r["Dispatch_Id"])
-        if "copy" in r["Kernel_Name"].lower() and d > last_copy[0]:
-            last_copy = (d, v)
-    return vals, last_copy[1]
+        if "copybuffer" in r["Kernel_Name"].lower():
+            big_copy = max(big_copy, v)
+    return vals, big_copy
 
 
 def hbm(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
