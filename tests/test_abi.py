@@ -223,3 +223,11 @@ def test_lm_head_verify_workspace_holds_the_verification_records(L):
     need = L.isd_lm_head_verify_workspace_bytes(64, 4, 151936)
     assert need > L.isd_verify_workspace_bytes(64, 4, 151936) > 0
     assert L.isd_lm_head_verify_workspace_bytes(0, 4, 151936) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback of any kind: without the built library every call raises."""
+    monkeypatch.setattr(isd, "_lib", None)
+    monkeypatch.setattr(isd, "_LIB_PATH", str(tmp_path / "libisd.so"))
+    with pytest.raises(RuntimeError, match="is not built"):
+        isd.lib()
