@@ -80,3 +80,9 @@ def test_qwen3_8b_full_size():
 def test_qwen3_32b_full_size():
     """B=64, 64 query / 8 KV heads, N=4, contexts ~ U[2048, 8192]; oracle on 3 requests."""
     run(synth.QWEN3_32B, sample=[0, 31, 63])
+
+
+def test_long_context_many_pieces():
+    """One 32000-token request next to a 5-token one: each long item is cut into ~64
+    pieces, so the combine stages its pieces in several chunks."""
+    run(step_cfg("long_ctx", "bf16", 2, 4, 32, 8, 128, 300), ctx_lens=[32000, 5], repeats=2)
