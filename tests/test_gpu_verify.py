@@ -49,6 +49,10 @@ CASES = [
     cfg("bf16_n8", "bf16", 6, 8, 20000, 17, noise_sd=0.1),
     cfg("bf16_argmax", "bf16", 16, 4, 33000, 18, argmax=True, noise_sd=0.05),
     cfg("f32_big_noise", "f32", 16, 4, 17000, 19, noise_sd=2.0),
+    # the largest vocabulary: 64 chunks, 1024 sub-chunk sums per row (past the walk's
+    # registers and its LDS stash, so those paths read them from memory)
+    cfg("bf16_v2pow20", "bf16", 2, 4, 1 << 20, 22),
+    cfg("bf16_v2pow20_argmax", "bf16", 2, 4, 1 << 20, 23, argmax=True, noise_sd=0.05),
 ]
 
 
