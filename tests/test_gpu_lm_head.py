@@ -101,6 +101,7 @@ FUSED_CASES = [
     (lcfg("b9_n1_v4000", 9, 1, 64, 4000, 55), False, ()),
     (lcfg("b3_n8_v33000", 3, 8, 64, 33000, 56), False, ()),
     (lcfg("b70_n4_v2048", 70, 4, 64, 2048, 57), False, ()),        # 490 rows: two row tiles
+    (lcfg("b2_n4_v2pow20", 2, 4, 32, 1 << 20, 64), False, ()),     # the largest vocabulary
 ]
 
 
