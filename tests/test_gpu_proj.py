@@ -45,9 +45,10 @@ def test_rlora_full_size():
 @pytest.mark.parametrize("M,K,Nout,r", [(1, 64, 128, 128), (130, 512, 256, 128),
                                         (7, 4096, 128, 256), (300, 1024, 640, 128),
                                         (448, 4096, 1024, 128), (7, 4096, 4096, 128),
-                                        (112, 12288, 4096, 128)])
+                                        (112, 12288, 4096, 128), (65536, 64, 128, 128)])
 def test_ragged_shapes(M, K, Nout, r):
-    """Includes shapes with few tiles, whose K is split over 2, 4 or 8 workgroups."""
+    """Includes shapes with few tiles, whose K is split over 2, 4 or 8 workgroups, and the
+    largest M (65536 rows, 1024 row tiles)."""
     run(M, K, Nout, r, 7 + M)
 
 
