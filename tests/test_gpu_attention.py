@@ -86,3 +86,11 @@ def test_long_context_many_pieces():
     """One 32000-token request next to a 5-token one: each long item is cut into ~64
     pieces, so the combine stages its pieces in several chunks."""
     run(step_cfg("long_ctx", "bf16", 2, 4, 32, 8, 128, 300), ctx_lens=[32000, 5], repeats=2)
+
+
+def test_most_requests_per_call():
+    """2048 requests (the bf16 path's limit), short ragged contexts: many items per
+    workgroup, the cost prefix at its full length; the oracle checks a sample."""
+    ctx = list(np.random.default_rng(5).integers(0, 41, 2048))
+    run(step_cfg("max_b", "bf16", 2048, 2, 8, 2, 64, 301), ctx_lens=ctx,
+        sample=[0, 1, 700, 1023, 1024, 2047])
