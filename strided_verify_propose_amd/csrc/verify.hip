@@ -13,7 +13,9 @@
 //            used exactly everywhere downstream, so every element weight has one rounding
 //            (the fma's) and no chunk carries a bias.  A resident grid walks the chunks
 //            with the next one's loads in flight (one workgroup per chunk when rows are not
-//            16-byte aligned).
+//            16-byte aligned).  It can cover a subset of each request's rows: in front of
+//            the LM head it takes only the draft rows, and the LM head's epilogue supplies
+//            the same records for the rows it computes.
 //   walk_residual  grid (chunks + 1, request) with sampled drafts, (1, request) with
 //            argmax drafts.  Every workgroup takes the request's walk from the chunk
 //            statistics in fp64 (row max, argmax, normaliser, acceptance); the last one
