@@ -13,7 +13,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libisd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attention.hip", "verify.hip", "commit.hip", "gemm.hip", "gemm_packed.hip", "lm_head.hip",
+SOURCES = ["attention.hip", "verify.hip", "commit.hip", "gemm.hip", "gemm_packed.hip", "gemm_big.hip",
+           "lm_head.hip",
            "isd_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -283,6 +283,7 @@ hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s) {
+  if (p.big) return launch_proj_big(p, false, s);
   base_kernel<<<grid_of(p.M, (p.Nout + p.r) * p.ksplit), THREADS, 0, s>>>(p);
   if (p.ksplit > 1) {
     const hipError_t e = launch_proj_reduce(p, s);

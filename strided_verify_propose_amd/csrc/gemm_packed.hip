@@ -213,6 +213,7 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
 }  // namespace
 
 hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s) {
+  if (p.big) return launch_proj_big(p, true, s);
   const int mt = (p.M + BM - 1) / BM;
   base_kernel_packed<<<tile_grid(mt, (p.Nout + p.r) / BN * p.ksplit), THREADS, 0, s>>>(p);
   if (p.ksplit > 1) {

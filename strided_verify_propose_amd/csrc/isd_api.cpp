@@ -99,12 +99,14 @@ LmhWs lmh_ws(int B, int N, int V) {
 // ---------------------------------------------------------------- projection workspace
 struct ProjWs {
   size_t ybase, T, part, total;
-  int ksplit;
+  int ksplit, big;
 };
 
 ProjWs proj_ws(int M, int K, int Nout, int r) {
   ProjWs w{};
-  w.ksplit = isd::proj_ksplit(M, K, Nout);
+  const int big_split = isd::proj_big_split(M, K, Nout);
+  w.big = big_split > 0;
+  w.ksplit = w.big ? big_split : isd::proj_ksplit(M, K, Nout);
   w.ybase = 0;
   w.T = align256(r > 0 ? (size_t)M * Nout * sizeof(float) : 0);
   w.part = w.T + align256((size_t)M * (r > 0 ? r : 0) * sizeof(uint16_t));
@@ -293,6 +295,7 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
   p.Y = static_cast<uint16_t*>(y);
   p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
   p.ksplit = ws_.ksplit;
+  p.big = ws_.big;
   p.part = ws ? reinterpret_cast<float*>(ws + ws_.part) : nullptr;
   if (lora) {
     p.A = static_cast<const uint16_t*>(a);
@@ -365,6 +368,7 @@ isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const u
   p.M = M; p.K = K; p.Nout = Nout; p.r = 0;
   p.Sp = pk;
   p.ksplit = ws_.ksplit;
+  p.big = ws_.big;
   p.part = ws ? reinterpret_cast<float*>(ws + ws_.part) : nullptr;
   if (lora) {
     p.gate = gate;

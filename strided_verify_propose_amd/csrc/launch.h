@@ -125,10 +125,15 @@ struct ProjLaunch {
   const uint16_t* Sp;           // packed path: [W^T; A^T] in fragment order
   int ksplit;                   // K split into this many equal parts (1: none)
   float* part;                  // workspace [ksplit][M][Nout + r] fp32 partial sums (ksplit > 1)
+  int big;                      // 224 x 256 tiles over ksplit ranges of whole k steps
 };
 // K split of the projection for few tiles: a function of (M, K, Nout) only, so that a
 // gated call and the base-only call on the same x, w split -- and round -- alike.
 int proj_ksplit(int M, int K, int Nout);
+// K ranges of the large-tile path, or 0 when the 64 x 128 kernels serve (M, K, Nout).
+int proj_big_split(int M, int K, int Nout);
+// Large-tile partial sums, their ordered sum, and the delta on gated rows.
+hipError_t launch_proj_big(const ProjLaunch& p, bool packed, hipStream_t s);
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s);
 hipError_t launch_lora(const ProjLaunch& p, hipStream_t s);  // the second kernel alone
 hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s);  // sum of the K parts

@@ -32,6 +32,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "lds_dma.h"
 #include "tiles.h"
 
 namespace isd {
@@ -56,18 +57,6 @@ constexpr int LROW = TBN + 8;       // LDS row stride of the epilogue tile, in b
 static_assert(BN == 128 && TBN == 2 * BN && TBM % 16 == 0, "tile shape: two mini-chunks per row");
 static_assert(VCHUNK % BN == 0 && VSUB % BN == 0, "mini-chunks tile the chunks");
 static_assert((size_t)TBM * LROW * 2 <= (size_t)RING * SLOT, "the epilogue tile fits in the ring");
-
-// s_waitcnt with only the vector-memory count bounded (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void load_frag(const uint16_t* src, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
 
 __global__ __launch_bounds__(THREADS, 1) void lmh_kernel(const LmhLaunch p) {
   const int mt = (p.M + TBM - 1) / TBM, nt = (p.NMINI + 1) / 2;

@@ -45,10 +45,14 @@ def test_rlora_full_size():
 @pytest.mark.parametrize("M,K,Nout,r", [(1, 64, 128, 128), (130, 512, 256, 128),
                                         (7, 4096, 128, 256), (300, 1024, 640, 128),
                                         (448, 4096, 1024, 128), (7, 4096, 4096, 128),
-                                        (112, 12288, 4096, 128), (65536, 64, 128, 128)])
+                                        (112, 12288, 4096, 128), (65536, 64, 128, 128),
+                                        (1300, 4096, 4096, 128), (448, 12288, 3072, 128),
+                                        (448, 6144, 6144, 256)])
 def test_ragged_shapes(M, K, Nout, r):
-    """Includes shapes with few tiles, whose K is split over 2, 4 or 8 workgroups, and the
-    largest M (65536 rows, 1024 row tiles)."""
+    """Includes shapes with few tiles, whose K is split over 2, 4 or 8 workgroups, the
+    largest M (65536 rows, 1024 row tiles), and the large-tile path: 224 x 256 tiles over 2
+    K ranges with a ragged last row tile (1300 rows), over 8 ranges (K = 12288), and over 4
+    with rank 256 (two column tiles of A^T rows)."""
     run(M, K, Nout, r, 7 + M)
 
 
@@ -77,16 +81,18 @@ def test_packed_layout():
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("M", [56, 448])
+@pytest.mark.parametrize("M", [56, 448, 1344])
 def test_back_to_back_calls_are_identical(M):
-    """Many calls in a row without synchronising, split-K (56 rows) and not (448 rows), on
-    both weight layouts: every result bitwise equal to the first.  Covers the order of the
-    first LDS refill against the waves' first fragment reads."""
+    """Many calls in a row without synchronising, on 64 x 128 tiles with K split (56 rows)
+    and without (448 rows), and on the large-tile path (1344 rows), on both weight layouts:
+    every result bitwise
+    equal to the first.  Covers the order of the first LDS refill against the waves' first
+    fragment reads."""
     cfg = synth.ProjConfig("b2b", B=8, N=4, K=4096, Nout=4096, r=128, x_sd=1.0, w_sd=0.02, seed=2030)
     p = synth.proj_inputs(cfg, M=M)
     x, w, a, b, g = (to_dev(t) for t in (p.x, p.w, p.a, p.b, p.gate))
     packed = isd.pack_proj_weights(w, a, b)
-    print(f"back-to-back projection M={M} ksplit path={'yes' if M < 64 else 'no'}", flush=True)
+    print(f"back-to-back projection M={M}", flush=True)
     for call in (lambda o: isd.gated_lora_proj(x, w, a, b, g, out=o),
                  lambda o: isd.gated_lora_proj_packed(x, packed, g, out=o)):
         outs = [torch.empty((M, cfg.Nout), dtype=torch.bfloat16, device="cuda") for _ in range(40)]
