@@ -53,34 +53,97 @@ __device__ __forceinline__ float row4_sum(float v) {
 }
 
 // ---------------------------------------------------------------- wave64 reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+// Butterfly over the 64 lanes without LDS: DPP quad permutes (lane ^ 1, lane ^ 2), row half
+// mirror and row mirror (eight and sixteen lanes), then the gfx950 row swaps across
+// 16-lane rows and 32-lane halves.  Every step combines a lane with a partner holding the
+// complementary lanes, and partners compute op(a, b) and op(b, a), so with a commutative op
+// every lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_mov<DPP_QUAD_XOR1>(v));
+  v = op(v, dpp_mov<DPP_QUAD_XOR2>(v));
+  v = op(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  v = op(v, dpp_mov<DPP_MIRROR>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(b[0], b[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_d(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = dpp_mov<CTRL>((uint32_t)u), hi = dpp_mov<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_mov_d<DPP_QUAD_XOR1>(v);
+  v += dpp_mov_d<DPP_QUAD_XOR2>(v);
+  v += dpp_mov_d<DPP_HALF_MIRROR>(v);
+  v += dpp_mov_d<DPP_MIRROR>(v);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
-  return v;
-}
-// Inclusive prefix sum over the 64 lanes (Hillis-Steele, lane order).
-__device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
+  for (int half = 0; half < 2; ++half) {
+    const uint64_t u = __double_as_longlong(v);
+    const auto lo = half ? __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false)
+                         : __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = half ? __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false)
+                         : __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+        __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
   }
   return v;
+}
+// Sum over each 16-lane row (every lane of the row gets it).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __uint_as_float(dpp_mov<DPP_QUAD_XOR1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_QUAD_XOR2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_HALF_MIRROR>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_MIRROR>(__float_as_uint(v)));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  return (int)wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return (uint32_t)min((int)a, (int)b); });
+}
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane row with DPP
+// row shifts (lanes shifted in from before the row read 0), then each row adds the totals
+// of the rows before it, read from lanes 15, 31 and 47.
+__device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
+  v += dpp_mov_d<0x111>(v);  // row_shr:1
+  v += dpp_mov_d<0x112>(v);  // row_shr:2
+  v += dpp_mov_d<0x114>(v);  // row_shr:4
+  v += dpp_mov_d<0x118>(v);  // row_shr:8
+  const uint64_t u = __double_as_longlong(v);
+  double tot[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, 16 * r + 15);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 16 * r + 15);
+    tot[r] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  const int row = lane >> 4;
+  double before = 0.0;  // sum of the earlier rows' totals, in row order
+  if (row >= 1) before = tot[0];
+  if (row >= 2) before += tot[1];
+  if (row >= 3) before += tot[2];
+  return v + before;
 }
 
 // ---------------------------------------------------------------- MFMA (CDNA4)

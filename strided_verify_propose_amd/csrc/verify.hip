@@ -122,10 +122,7 @@ __device__ __forceinline__ void sub_sums(const float (&s)[ROUNDS], float* lds, f
   float v = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) v += src[i];
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 1);
+  v = row16_sum(v);
   const int sub = chunk * SUBS + j;
   if (p == 0 && sub < nsub) out[sub] = v;
 }
@@ -285,10 +282,7 @@ __device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, i
     float vv = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) vv += src[i];
-    vv += __shfl_xor(vv, 8);
-    vv += __shfl_xor(vv, 4);
-    vv += __shfl_xor(vv, 2);
-    vv += __shfl_xor(vv, 1);
+    vv = row16_sum(vv);
     const int sub = chunk * VCHUNK_SUBS + j;
     if (p == 0 && sub < v.NSUB) v.csub[(size_t)rowid * v.NSUB + sub] = vv;
   }
