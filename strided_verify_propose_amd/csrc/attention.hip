@@ -21,7 +21,7 @@
 //     unnormalised partial (max, sum, O) for the at most two items cut by its share's
 //     edges; a second kernel merges those in workgroup order and appends the block's K/V
 //     to the cache after all reads.  No workgroup waits on or signals another.
-//   * Inside a workgroup the four waves take the tiles of a piece round-robin (the
+//   * Inside a workgroup the group's waves take the tiles of a piece round-robin (the
 //     block's own rows and the partial page first), keep the next page's loads in flight
 //     while using the current one, and merge their states through LDS in a fixed order,
 //     each wave combining and writing a quarter of the head dimension.
@@ -43,15 +43,17 @@ __device__ __forceinline__ int page_id(const int32_t* pt, int j, int num_pages) 
   return min(max(pt[j], 0), num_pages - 1);
 }
 
-// Query rows handled per wave and wave groups per workgroup.  Each wave keeps up to two
-// 16-row query blocks in registers; with more blocks (many query heads per KV head) a
-// second group of four waves takes the rest and reads the same pages, the repeats
-// hitting cache.
-template <int NQB>
+// Query rows handled per wave, waves per group and wave groups per workgroup.  Each wave
+// keeps up to two 16-row query blocks in registers.  With at most two blocks one group of
+// eight waves deals the pages (one workgroup per CU, so no CU splits its time between two
+// workgroups); with more blocks (many query heads per KV head) two groups of four waves
+// each take half of them and read the same pages, the repeats hitting cache.
+template <int D, int NQB>
 struct AttnShape {
   static constexpr int QB = NQB < 2 ? NQB : 2;
   static constexpr int GROUPS = (NQB + QB - 1) / QB;
-  static constexpr int THREADS = 256 * GROUPS;
+  static constexpr int WPG = (GROUPS == 1 && D / 16 >= 8) ? 8 : 4;  // waves per group
+  static constexpr int THREADS = 64 * WPG * GROUPS;
 };
 
 // One 16-token tile (a cached page or the block) against this wave's query blocks.
@@ -206,15 +208,17 @@ __device__ __forceinline__ int range_lo(int w, int T, int W) {
 }
 
 template <int D, int NQB>
-__global__ __launch_bounds__(AttnShape<NQB>::THREADS, 2)
+__global__ __launch_bounds__((AttnShape<D, NQB>::THREADS), 2)
 void attn_bf16_kernel(const AttnLaunch a) {
-  constexpr int QB = AttnShape<NQB>::QB;
-  constexpr int GROUPS = AttnShape<NQB>::GROUPS;
+  constexpr int QB = AttnShape<D, NQB>::QB;
+  constexpr int GROUPS = AttnShape<D, NQB>::GROUPS;
+  constexpr int WPG = AttnShape<D, NQB>::WPG;
   constexpr int STATE = state_floats<D, QB>();
   constexpr int NB = D / 16;           // 16-dim output blocks
-  constexpr int NPW = NB / 4;          // output blocks merged and written per wave
+  constexpr int NPW = NB / WPG;        // output blocks merged and written per wave
+  static_assert(NPW * WPG == NB, "the group's waves split the output blocks evenly");
   __shared__ int pre[MAX_B + 1];
-  __shared__ float st_buf[GROUPS][4][STATE];
+  __shared__ float st_buf[GROUPS][WPG][STATE];
 
   build_prefix(a, pre);
   const int T = pre[a.B];
@@ -223,7 +227,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
 
   const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = wave >> 2, wg = wave & 3;  // wave group, wave within the group
+  const int grp = wave / WPG, wg = wave % WPG;  // wave group, wave within the group
   const int qb0 = grp * QB;                  // this group's first query block
   const int l16 = lane & 15, g = lane >> 4;
   const float scale_log2 = a.scale * 1.4426950408889634f;
@@ -254,14 +258,14 @@ void attn_bf16_kernel(const AttnLaunch a) {
 
     // The piece's units in a fixed order -- the block's own rows (unit ncp) and the
     // partial page (unit nfull) first, then the full pages ascending -- dealt round-robin
-    // to the four waves, so that every wave holds the same number of tiles.
+    // to the group's waves, so that every wave holds the same number of tiles.
     const bool has_block = unit0 <= ncp && ncp < unit1;
     const bool has_partial = nfull < ncp && unit0 <= nfull && nfull < unit1;
     const int nspecial = (has_block ? 1 : 0) + (has_partial ? 1 : 0);
     const bool do_block = has_block && wg == 0;
     const bool do_partial = has_partial && wg == (has_block ? 1 : 0);
     const int fend = min(unit1, nfull);  // full pages of the piece: [unit0, fend)
-    int c0 = unit0 + (wg < nspecial ? wg + 4 - nspecial : wg - nspecial);  // this wave's first
+    int c0 = unit0 + (wg < nspecial ? wg + WPG - nspecial : wg - nspecial);  // this wave's first
 
     // Issue first what needs no page id: Q^T fragments (B operand of S^T = K Q^T), the
     // page ids of this wave's first 64 full pages, the partial page's id, the block rows.
@@ -278,13 +282,13 @@ void attn_bf16_kernel(const AttnLaunch a) {
       for (int c = 0; c < D / 32; ++c)
         qf[j][c] = *reinterpret_cast<const u32x4*>(q + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 32 * c + 8 * g);
     }
-    int my_id = page_id(pt, min(c0 + 4 * lane, a.max_pages - 1), a.num_pages);
+    int my_id = page_id(pt, min(c0 + WPG * lane, a.max_pages - 1), a.num_pages);
 #pragma unroll
     for (int j = 0; j < QB; ++j)
       if (qb0 + j >= NQB || (qb0 + j) * 16 + l16 >= RG)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) qf[j][c] = u32x4{0u, 0u, 0u, 0u};
-    if (c0 + 4 * lane >= fend) my_id = 0;
+    if (c0 + WPG * lane >= fend) my_id = 0;
 
     f32x4 o[QB][D / 16];
     float m[QB], l[QB];
@@ -336,10 +340,10 @@ void attn_bf16_kernel(const AttnLaunch a) {
     // register buffers: the next page's loads are issued before the current page is
     // used, and a scheduling barrier keeps them there.  Loads inside the loop are
     // unconditional, so the compiler's wait counts stay exact (the tail is peeled).
-    for (; c0 < fend; c0 += 256) {
-      const int nu = min(64, (fend - c0 + 3) / 4);
+    for (; c0 < fend; c0 += 64 * WPG) {
+      const int nu = min(64, (fend - c0 + WPG - 1) / WPG);
       size_t t;
-      if (c0 != unit0 + (wg < nspecial ? wg + 4 - nspecial : wg - nspecial)) {
+      if (c0 != unit0 + (wg < nspecial ? wg + WPG - nspecial : wg - nspecial)) {
         t = page_off(__builtin_amdgcn_readlane(my_id, 0));
         load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
       }
@@ -363,15 +367,15 @@ void attn_bf16_kernel(const AttnLaunch a) {
       } else {
         attend_tile<D, QB, 0>(kf, vf, qf, qb0, NQB, o, m, l, scale_log2, PAGE, G, lane);
       }
-      if (c0 + 256 < fend) {
-        my_id = page_id(pt, min(c0 + 256 + 4 * lane, a.max_pages - 1), a.num_pages);
-        if (c0 + 256 + 4 * lane >= fend) my_id = 0;
+      if (c0 + 64 * WPG < fend) {
+        my_id = page_id(pt, min(c0 + 64 * WPG + WPG * lane, a.max_pages - 1), a.num_pages);
+        if (c0 + 64 * WPG + WPG * lane >= fend) my_id = 0;
       }
     }
 
-    // Merge the group's four wave states: all four go to LDS, then wave k of the group
-    // combines output blocks [k NPW, (k+1) NPW) of every query row over the waves in the
-    // order 0, 1, 2, 3, and writes them.
+    // Merge the group's wave states: all of them go to LDS, then wave k of the group
+    // combines output blocks [k NPW, (k+1) NPW) of every query row over the waves in
+    // wave order, and writes them.
 #pragma unroll
     for (int j = 0; j < QB; ++j) l[j] = row4_sum(l[j]);
     stash_state<D, QB>(o, m, l, st_buf[grp][wg], lane);
@@ -384,16 +388,16 @@ void attn_bf16_kernel(const AttnLaunch a) {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int qr = (qb0 + j) * 16 + l16;
-      float mw[4], fw[4];
+      float mw[WPG], fw[WPG];
       float M = neg_inf();
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < WPG; ++k) {
         mw[k] = st_buf[grp][k][(j * 2) * 64 + lane];
         M = fmaxf(M, mw[k]);
       }
       float Lsum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < WPG; ++k) {
         fw[k] = (mw[k] == neg_inf()) ? 0.f : exp2_hw(mw[k] - M);
         Lsum += fw[k] * st_buf[grp][k][(j * 2 + 1) * 64 + lane];
       }
@@ -404,7 +408,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
         const int n = wg * NPW + nn;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < WPG; ++k)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[i] += fw[k] * st_buf[grp][k][(2 * QB + (j * (D / 16) + n) * 4 + i) * 64 + lane];
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(THREADS) void attn_f32_kernel(const AttnLaunch a) {
 
 template <int D, int NQB>
 hipError_t launch_shape(const AttnLaunch& a, hipStream_t s) {
-  constexpr int NT = AttnShape<NQB>::THREADS;
+  constexpr int NT = AttnShape<D, NQB>::THREADS;
   // one workgroup per resident slot (every slot gets an equal share of tiles), fewer
   // when the work is small; the slot count is queried once per device
   static std::atomic<int> slots_of_device[64];
