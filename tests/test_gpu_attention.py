@@ -67,6 +67,8 @@ RAGGED = [0, 1, 15, 16, 17, 31, 511, 512, 513, 1100, 2047]
     ("g2_d64_n3", 3, 8, 4, 64),
     ("g4_d64_n1", 1, 16, 4, 64),
     ("g4_d128_n8_60rows", 8, 8, 2, 128),
+    ("g6_d128_n4_three_blocks", 4, 48, 8, 128),  # two wave groups, the second with one block
+    ("g4_d128_n2_one_block", 2, 32, 8, 128),     # 12 query rows: one block over eight waves
 ])
 def test_bf16_ragged_contexts(name, N, Hq, Hkv, D):
     run(step_cfg(name, "bf16", len(RAGGED), N, Hq, Hkv, D, 200 + N), ctx_lens=RAGGED, repeats=2)
