@@ -14,8 +14,9 @@
 // With the weights in that order every wave loads its B operands straight from memory
 // with 1 KB fully coalesced loads, and only the activation tile goes through LDS (stored
 // as fragments with the same conflict-free xor swizzle as the row-major kernels).
-// Tiles: 64 x 128 per workgroup, 4 waves of 64 x 32 (4 x 2 MFMA 16x16x32 blocks), K in
-// steps of 64 with three steps of loads in flight.
+// Tiles: 64 x 128 per workgroup, 8 waves of 64 x 16 (4 x 1 MFMA 16x16x32 blocks) when the
+// grid is one round, else 4 waves of 64 x 32 (4 x 2 blocks); K in steps of 64 with three
+// steps of loads in flight.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -24,9 +25,7 @@ namespace isd {
 namespace {
 
 constexpr int BM = 64, BN = 128, BK = 64;
-constexpr int THREADS = 256;
 constexpr int RING = 4;                         // register stages of the load pipeline
-constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte activation loads per thread per k step
 constexpr int FRAG = 64 * 8;                    // elements in one packed 16 x 32 fragment
 
 // ---------------------------------------------------------------- packing
@@ -55,9 +54,21 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- product
+// The tile's 128 columns are split over WAVES waves (4: 32 columns each, 8: 16 each).
+// Every output element gets the same MFMA sequence either way, so the results do not
+// depend on the wave count; 8 waves hide more latency when the grid is one round.
+template <int WAVES>
+struct Shape {
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int CBW = BN / 16 / WAVES;            // column blocks per wave
+  static constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte activation loads per thread per k step
+  static constexpr int ROWS = THREADS / 8;               // activation rows per load round
+};
+
+template <int WAVES>
 struct Stage {
-  u32x4 a[A_LOADS];
-  u32x4 b[2][2];  // this wave's weight fragments [column block][k half]
+  u32x4 a[Shape<WAVES>::A_LOADS];
+  u32x4 b[Shape<WAVES>::CBW][2];  // this wave's weight fragments [column block][k half]
 };
 
 // LDS activation tile: MFMA fragments [k half][16-row block][slot].  Row r, 16-byte k chunk
@@ -68,22 +79,24 @@ struct ATile {
 
 __device__ __forceinline__ int chunk_slot(int r, int c) { return (c & 3) * 16 + ((r & 15) ^ c); }
 
-__device__ __forceinline__ void issue(Stage& st, const uint16_t* const (&pa)[A_LOADS],
-                                      const uint16_t* const (&pb)[2], int s) {
+template <int WAVES>
+__device__ __forceinline__ void issue(Stage<WAVES>& st, const uint16_t* const (&pa)[Shape<WAVES>::A_LOADS],
+                                      const uint16_t* const (&pb)[Shape<WAVES>::CBW], int s) {
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(pa[i] + s * BK);
+  for (int i = 0; i < Shape<WAVES>::A_LOADS; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(pa[i] + s * BK);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < Shape<WAVES>::CBW; ++cb)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       st.b[cb][kk] = *reinterpret_cast<const u32x4*>(pb[cb] + (size_t)(2 * s + kk) * FRAG);
 }
 
-__device__ __forceinline__ void put(ATile& t, const Stage& st, int tid) {
+template <int WAVES>
+__device__ __forceinline__ void put(ATile& t, const Stage<WAVES>& st, int tid) {
   const int c = tid & 7;
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+  for (int i = 0; i < Shape<WAVES>::A_LOADS; ++i) {
+    const int r = (tid >> 3) + Shape<WAVES>::ROWS * i;
     t.f[c >> 2][r >> 4][chunk_slot(r, c)] = st.a[i];
   }
 }
@@ -101,45 +114,50 @@ __device__ __forceinline__ void fetch_frags(Frags& f, const ATile& t, int lane) 
   }
 }
 
-__device__ __forceinline__ void mma(const Frags& f, const Stage& st, f32x4 (&acc)[BM / 16][2]) {
+template <int WAVES>
+__device__ __forceinline__ void mma(const Frags& f, const Stage<WAVES>& st,
+                                    f32x4 (&acc)[BM / 16][Shape<WAVES>::CBW]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int rb = 0; rb < BM / 16; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma16x16x32(f.a[kk][rb], st.b[cb][kk], acc[rb][cb]);
+      for (int cb = 0; cb < Shape<WAVES>::CBW; ++cb)
+        acc[rb][cb] = mfma16x16x32(f.a[kk][rb], st.b[cb][kk], acc[rb][cb]);
 }
 
-// acc[rb][cb] = sum over k < K of X[16 rb + row][k] S[32 wave + 16 cb + col][k] for the
+// acc[rb][cb] = sum over k < K of X[16 rb + row][k] S[16 (CBW wave + cb) + col][k] for the
 // 64 x 128 tile at X and the packed fragments at Sp (the tile's first 16-column block, at
 // the first k of the part; Kfull is the weights' full K).
 // X rows past `mrows` read row mrows - 1 (never stored).  At step s: loads for step
 // s + RING - 1 go out, step s + 2's activations go to LDS, step s + 1's activation
 // fragments come from LDS, and step s's MFMAs run.
+template <int WAVES>
 __device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int ldx, int mrows,
                           const uint16_t* __restrict__ Sp, int Kfull, int K, int tid, int wave, int lane,
-                          f32x4 (&acc)[BM / 16][2]) {
+                          f32x4 (&acc)[BM / 16][Shape<WAVES>::CBW]) {
   static_assert(RING % 2 == 0 && RING >= 4, "fragment buffers alternate with the step parity");
+  constexpr int A_LOADS = Shape<WAVES>::A_LOADS, CBW = Shape<WAVES>::CBW;
   const int KB = Kfull / 32;  // fragments per 16-column block of the packed weights
   const uint16_t* pa[A_LOADS];
-  const uint16_t* pb[2];
+  const uint16_t* pb[CBW];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i)
-    pa[i] = X + (size_t)min((tid >> 3) + 32 * i, mrows - 1) * ldx + (tid & 7) * 8;
+    pa[i] = X + (size_t)min((tid >> 3) + Shape<WAVES>::ROWS * i, mrows - 1) * ldx + (tid & 7) * 8;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) pb[cb] = Sp + ((size_t)(2 * wave + cb) * KB) * FRAG + lane * 8;
+  for (int cb = 0; cb < CBW; ++cb) pb[cb] = Sp + ((size_t)(CBW * wave + cb) * KB) * FRAG + lane * 8;
 #pragma unroll
   for (int rb = 0; rb < BM / 16; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CBW; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int S = K / BK;
-  Stage r[RING];
+  Stage<WAVES> r[RING];
   Frags f[2];
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) issue(r[u], pa, pb, min(u, S - 1));
-  put(lds[0], r[0], tid);
-  put(lds[1], r[1], tid);
+  for (int u = 0; u < RING - 1; ++u) issue<WAVES>(r[u], pa, pb, min(u, S - 1));
+  put<WAVES>(lds[0], r[0], tid);
+  put<WAVES>(lds[1], r[1], tid);
   lds_barrier();
   fetch_frags(f[0], lds[0], lane);
   lds_barrier();  // every wave has read buffer 0 before step 0 refills it with step 2
@@ -149,16 +167,18 @@ __device__ void gemm_tile(ATile (&lds)[2], const uint16_t* __restrict__ X, int l
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       const int s = s0 + u;
-      issue(r[(u + RING - 1) % RING], pa, pb, min(s + RING - 1, S - 1));
+      issue<WAVES>(r[(u + RING - 1) % RING], pa, pb, min(s + RING - 1, S - 1));
       fetch_frags(f[(u + 1) & 1], lds[(s + 1) & 1], lane);
-      put(lds[s & 1], r[(u + 2) % RING], tid);
-      if (s < S) mma(f[u & 1], r[u], acc);
+      put<WAVES>(lds[s & 1], r[(u + 2) % RING], tid);
+      if (s < S) mma<WAVES>(f[u & 1], r[u], acc);
       lds_barrier();
     }
   }
 }
 
-__global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p) {
+template <int WAVES>
+__global__ __launch_bounds__(Shape<WAVES>::THREADS) void base_kernel_packed(const ProjLaunch p) {
+  constexpr int CBW = Shape<WAVES>::CBW;
   const int mt = (p.M + BM - 1) / BM, nt = (p.Nout + p.r) / BN;
   int tm, tn;
   if (!tile_of(blockIdx.x, mt, nt * p.ksplit, tm, tn)) return;
@@ -171,8 +191,8 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
   const bool lowrank = n0 >= p.Nout;  // this tile computes T = X A
   const size_t blk = (size_t)(p.K / 32) * FRAG;  // elements per packed 16-column block
   __shared__ ATile lds[2];
-  f32x4 acc[BM / 16][2];
-  gemm_tile(lds, p.X + (size_t)m0 * p.K + k0, p.K, mrows, p.Sp + (size_t)(n0 / 16) * blk + (size_t)(k0 / 32) * FRAG,
+  f32x4 acc[BM / 16][CBW];
+  gemm_tile<WAVES>(lds, p.X + (size_t)m0 * p.K + k0, p.K, mrows, p.Sp + (size_t)(n0 / 16) * blk + (size_t)(k0 / 32) * FRAG,
             p.K, klen, tid, wave, lane, acc);
   if (p.ksplit > 1) {  // partial sums; the reduce kernel adds them in order and stores
     const int ncols = p.Nout + p.r;
@@ -183,8 +203,8 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
         const int row = rb * 16 + 4 * gq + e;
         if (row >= mrows) continue;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          p.part[((size_t)ks * p.M + m0 + row) * ncols + n0 + wave * 32 + cb * 16 + l16] = acc[rb][cb][e];
+        for (int cb = 0; cb < CBW; ++cb)
+          p.part[((size_t)ks * p.M + m0 + row) * ncols + n0 + wave * 16 * CBW + cb * 16 + l16] = acc[rb][cb][e];
       }
     return;
   }
@@ -197,8 +217,8 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
       const int gr = m0 + row;
       const bool gated = p.gate != nullptr && p.gate[gr] != 0;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int col = n0 + wave * 32 + cb * 16 + l16;
+      for (int cb = 0; cb < CBW; ++cb) {
+        const int col = n0 + wave * 16 * CBW + cb * 16 + l16;
         const float v = acc[rb][cb][e];
         if (lowrank)
           p.T[(size_t)gr * p.r + (col - p.Nout)] = (uint16_t)f32_to_bf16_bits(v);
@@ -214,8 +234,13 @@ __global__ __launch_bounds__(THREADS) void base_kernel_packed(const ProjLaunch p
 
 hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s) {
   if (p.big) return launch_proj_big(p, true, s);
-  const int mt = (p.M + BM - 1) / BM;
-  base_kernel_packed<<<tile_grid(mt, (p.Nout + p.r) / BN * p.ksplit), THREADS, 0, s>>>(p);
+  const int mt = (p.M + BM - 1) / BM, tiles = mt * (p.Nout + p.r) / BN * p.ksplit;
+  // eight waves per tile when every tile gets a CU of its own (at most one workgroup of
+  // 8 waves is resident per CU), else four, two workgroups sharing a CU
+  if (tiles <= 256)
+    base_kernel_packed<8><<<tile_grid(mt, (p.Nout + p.r) / BN * p.ksplit), Shape<8>::THREADS, 0, s>>>(p);
+  else
+    base_kernel_packed<4><<<tile_grid(mt, (p.Nout + p.r) / BN * p.ksplit), Shape<4>::THREADS, 0, s>>>(p);
   if (p.ksplit > 1) {
     const hipError_t e = launch_proj_reduce(p, s);
     if (e != hipSuccess) return e;
