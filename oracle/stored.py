@@ -23,3 +23,16 @@ def round_bf16(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """Stored bf16 bit patterns (uint16) of float64 values that are already bf16 values
+    (e.g. the output of round_bf16): the float32 of such a value is exact, and its upper
+    half is the pattern."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64)):
+        raise ValueError("to_bf16_bits: value is not a bf16 value")
+    bits = x32.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("to_bf16_bits: value is not a bf16 value")
+    return (bits >> 16).astype(np.uint16)

@@ -86,6 +86,16 @@ def inverse_cdf(w, u):
     return k, lo, c[k] / total
 
 
+def expected_acceptance(anchor_logits, draft_logits, temperature=1.0):
+    """Probability that a draft d ~ q~ passes the test u < min(1, p(d)/q~(d)):
+    sum_d q~(d) min(1, p(d)/q~(d)) = sum_k min(p_k, q~_k), with p = softmax(anchor/T) and
+    q~ = softmax(draft/T) of one row each.  This is the acceptance rate p of the
+    tokens-per-forward formula for i.i.d. rows."""
+    _, p = log_softmax_row(to_f64(anchor_logits) / float(temperature))
+    _, q = log_softmax_row(to_f64(draft_logits) / float(temperature))
+    return float(np.sum(np.minimum(p, q)))
+
+
 def verify(logits, draft_logits, draft_ids, uniforms, N, temperature=1.0, eps=1e-6):
     """One verification step for B requests.  Returns a dict of NumPy arrays:
 
@@ -177,13 +187,6 @@ def verify(logits, draft_logits, draft_ids, uniforms, N, temperature=1.0, eps=1e
             res["residual_flag"][b] = (abs(u - (a + (1 - a) * lo)) < eps or
                                        abs(u - (a + (1 - a) * hi)) < eps)
     return res
-
-
-def emitted_tokens(res, draft_ids, b):
-    """Tokens a request commits this step: accepted drafts, then the next token (a cold
-    request accepts none)."""
-    n = int(res["n_accept"][b])
-    return [int(t) for t in draft_ids[b, :n]] + [int(res["next_token"][b])]
 
 
 def commit(n_accept, next_token, sampled_ids, draft_ids, ctx_lens, N):

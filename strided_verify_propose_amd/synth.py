@@ -110,6 +110,22 @@ PROJ = ProjConfig("rlora_448x4096x4096_r128", B=64, N=4, K=4096, Nout=4096, r=12
                   x_sd=1.0, w_sd=0.02, seed=1004)
 
 
+# Proposal noise sd of the sweep for mean acceptance 0.5 and 0.9 (anchors N(0, 3),
+# vocabulary 151936), bisected on the oracle by tests/golden/sweep_sigma.py.
+SWEEP_SIGMA = {0.5: 1.367109, 0.9: 0.255684}
+SWEEP_B = (1, 4, 16, 64)
+
+
+def sweep_index(N: int, B: int, p: float) -> int:
+    """Sweep point index, lexicographic in (N, B, p): N in {2,3,4}, B in SWEEP_B, p in {0.5, 0.9}."""
+    return ((N - 2) * len(SWEEP_B) + SWEEP_B.index(B)) * 2 + (0 if p == 0.5 else 1)
+
+
+def sweep_point(N: int, B: int, p: float) -> StepConfig:
+    """The sweep point (N, B, p) with its calibrated noise and seed 1200 + index."""
+    return sweep_config(N, B, SWEEP_SIGMA[p], sweep_index(N, B, p))
+
+
 def sweep_config(N: int, B: int, noise_sd: float, index: int) -> StepConfig:
     """Stride/concurrency sweep point on the Qwen3-8B shapes at fixed context 2048."""
     return StepConfig(f"sweep_n{N}_b{B}", "bf16", B=B, N=N, Hq=32, Hkv=8, D=128, V=151936,
@@ -357,3 +373,66 @@ def lm_head_inputs(cfg: LmHeadConfig, seed: int | None = None, argmax_drafts: bo
         draft_logits = draft_stored
     u = uniforms24(g["uniforms"], (B, R))
     return LmHeadInputs(cfg, hidden, w_lm, draft_logits, draft_ids, u)
+
+
+# ----------------------------------------------------------------------------- decoder layer
+@dataclass
+class LayerInputsConfig:
+    """An R-ISD decoder layer of a Qwen3-shaped model over one strided block: seven
+    linears (q, k, v, o, gate, up, down) each with a rank-r delta, and the block's
+    attention over a paged cache.  Qwen3-8B: hidden 4096, 32 query heads, 8 KV heads,
+    head dim 128, intermediate 12288."""
+    name: str
+    B: int
+    N: int
+    hidden: int
+    Hq: int
+    Hkv: int
+    D: int
+    inter: int
+    r: int
+    ctx: tuple          # ('fixed', L) or ('uniform', lo, hi) inclusive
+    seed: int
+
+    @property
+    def R(self) -> int:
+        return 2 * self.N - 1
+
+    @property
+    def M(self) -> int:
+        return self.B * self.R
+
+    def shapes(self) -> dict:
+        """(K, Nout) of each linear."""
+        H, I = self.hidden, self.inter
+        return dict(q=(H, self.Hq * self.D), k=(H, self.Hkv * self.D), v=(H, self.Hkv * self.D),
+                    o=(self.Hq * self.D, H), gate=(H, I), up=(H, I), down=(I, H))
+
+
+@dataclass
+class LayerInputs:
+    cfg: LayerInputsConfig
+    x: np.ndarray               # [M, hidden] bf16 bits, request-major
+    weights: dict               # name -> (w [Nout, K], a [r, K], b [Nout, r]) bf16 bits
+    gate: np.ndarray            # [M] uint8: 0 on the N-1 verify rows, 1 on the others
+    attn: AttentionInputs       # cache, page table, context lengths (its q/k/v unused)
+
+
+def layer_inputs(cfg: LayerInputsConfig) -> LayerInputs:
+    """x ~ N(0, 1); w, a ~ N(0, 1/K) (sd 1/sqrt(K)); b ~ N(0, 0.02); cached K/V ~ N(0, 1)
+    in seeded pages (as attention_inputs).  The N-1 verify rows of each block are
+    ungated, the bonus row and the [MASK] rows gated."""
+    g = streams(cfg.seed)
+    step = StepConfig(cfg.name, "bf16", B=cfg.B, N=cfg.N, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, V=2,
+                      ctx=cfg.ctx, anchor_sd=1.0, noise_sd=1.0, seed=cfg.seed + 1)
+    attn = attention_inputs(step)
+    x = bf16_rne(normal(g["x"], (cfg.M, cfg.hidden), 1.0))
+    weights = {}
+    for name, (K, Nout) in cfg.shapes().items():
+        sd = 1.0 / math.sqrt(K)
+        w = bf16_rne(normal(g["w"], (Nout, K), sd))
+        a = bf16_rne(normal(g["a"], (cfg.r, K), sd))
+        b = bf16_rne(normal(g["b"], (Nout, cfg.r), 0.02))
+        weights[name] = (w, a, b)
+    gate = np.resize(np.array([0] * (cfg.N - 1) + [1] * cfg.N, np.uint8), cfg.M)
+    return LayerInputs(cfg, x, weights, gate, attn)

@@ -101,3 +101,26 @@ def test_lm_head_wrong_weight_column_is_caught(monkeypatch):
     monkeypatch.setattr(olm, "lm_head_logits",
                         lambda h, w: olm.round_bf16(olm.to_f64(h) @ np.roll(olm.to_f64(w), 1, axis=1).T))
     fails(t_lm.test_one_hot_rows_pick_one_weight_each)
+
+
+def test_layer_sigmoid_for_silu_is_caught(monkeypatch):
+    import oracle.layer as olay
+    from tests import test_oracle_layer as t_lay
+    monkeypatch.setattr(olay, "silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64))))
+    fails(t_lay.test_layer_matches_brute_force, 11, True)
+
+
+def test_layer_dropped_residual_is_caught(monkeypatch):
+    import oracle.layer as olay
+    from tests import test_oracle_layer as t_lay
+    monkeypatch.setattr(olay, "residual", lambda x, y: olay.round_bf16(y))   # h = o(att), no x
+    fails(t_lay.test_layer_matches_brute_force, 12, True)
+
+
+def test_layer_swapped_gate_and_up_is_caught(monkeypatch):
+    import oracle.layer as olay
+    from tests import test_oracle_layer as t_lay
+    orig = olay.linear
+    swap = {"gate": "up", "up": "gate"}
+    monkeypatch.setattr(olay, "linear", lambda y, w, name, g: orig(y, w, swap.get(name, name), g))
+    fails(t_lay.test_layer_matches_brute_force, 11, True)
