@@ -20,6 +20,8 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
  *     the default stream).  Nothing is synchronised; outputs are ready when the stream is.
  *   - Shapes, dtypes and pointers are checked on the host before anything is launched.
+ *     The *_workspace_bytes and *_bytes queries return 0 for shapes their entry point
+ *     does not accept.
  *     A failed check returns ISD_ERR_INVALID_ARG (bad value), ISD_ERR_UNSUPPORTED (valid
  *     but outside what the kernels implement) or ISD_ERR_WORKSPACE (too small), and
  *     launches nothing.  A failed launch returns ISD_ERR_HIP.  isd_last_error() then
@@ -86,10 +88,12 @@ const char* isd_last_error(void);
  *   KV head h / G.  The block's own keys are used as written, so the result equals attention
  *   read entirely through the pages after the append.  Rejected tokens are rolled back by the
  *   caller simply not advancing ctx_lens; their slots are overwritten by the next step.
- * Requires: page_size == 16, D in {64, 128}, Hq % Hkv == 0,
+ * Requires: page_size == 16, D in {64, 128}, Hq % Hkv == 0, Hq <= 65535,
  *   every page the request touches (ctx_lens[b]+R tokens) present in its page table,
  *   0 <= ctx_lens[b] <= max_ctx_len, max_ctx_len + R <= 16*max_pages_per_seq;
- *   for ISD_BF16 also R*G <= 64, N <= 8 and B <= 2048; for ISD_F32 max_ctx_len + R <= 16384.
+ *   for ISD_BF16 also R*G <= 64, N <= 8, B <= 2048 and
+ *   B*Hkv*(ceil(max_ctx_len/16) + 25) <= 2^31 - 1 (the work list's cost units, else
+ *   ISD_ERR_UNSUPPORTED); for ISD_F32 max_ctx_len + R <= 16384.
  * scale: usually 1/sqrt(D).  Workspace: isd_attention_workspace_bytes (bf16 only; the
  *   f32 path needs none). */
 size_t isd_attention_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_ctx_len);
@@ -169,7 +173,8 @@ isd_status isd_commit(const int32_t* n_accept, const int32_t* next_token, const 
  *   gate [M] uint8 in {0, 1}; NULL => base-only (a and b may then be NULL)
  * Computes y = x W + gate * (bf16(x A)) B, rounded to bf16.  Rows with gate 0 are
  * bit-identical to the base-only call on the same x, w.
- * Requires: K % 64 == 0, Nout % 128 == 0, r in {128, 256} when gated, 1 <= M <= 65536. */
+ * Requires: K % 64 == 0 and 64 <= K <= 2^20, Nout % 128 == 0 and 128 <= Nout <= 2^20,
+ * r in {128, 256} when gated, 1 <= M <= 65536. */
 size_t isd_gated_lora_workspace_bytes(int M, int K, int Nout, int r);
 isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, const void* b,
                                const uint8_t* gate, void* y, int M, int K, int Nout, int r,
@@ -190,8 +195,9 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
  *   (a, b unused when r == 0); asynchronous on `stream`.
  * isd_gated_lora_proj_packed: as isd_gated_lora_proj with the packed buffer in place of
  *   w, a, b; r is the rank the buffer was packed with (gate NULL => base only, any r).
- * Requires: K % 64 == 0, Nout % 128 == 0, r in {0, 128, 256}, r > 0 when gated,
- *   1 <= M <= 65536.  Workspace: isd_gated_lora_workspace_bytes(M, K, Nout, r). */
+ * Requires: K % 64 == 0 and 64 <= K <= 2^20, Nout % 128 == 0 and 128 <= Nout <= 2^20,
+ *   r in {0, 128, 256}, r > 0 when gated, 1 <= M <= 65536.
+ *   Workspace: isd_gated_lora_workspace_bytes(M, K, Nout, r). */
 size_t isd_proj_packed_bytes(int K, int Nout, int r);
 isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, void* packed, int K,
                                  int Nout, int r, void* stream);

@@ -34,7 +34,7 @@
 namespace isd {
 namespace {
 
-constexpr int PAGE = 16;
+constexpr int PAGE = ATTN_PAGE;
 constexpr int THREADS = 256;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
@@ -158,8 +158,8 @@ __device__ __forceinline__ void stash_state(const f32x4 (&o)[QB][D / 16], const 
 // and its real units sit at [s + ITEM_COST, s + ITEM_COST + u_b).  Workgroup w of a grid
 // of W takes cost [w T / W, (w+1) T / W), so every workgroup gets the same estimated time
 // whatever the spread of context lengths and however many items its range touches.
-constexpr int MAX_B = 2048;    // requests per call on the bf16 path (prefix kept in LDS)
-constexpr int ITEM_COST = 24;  // start-up cost of a piece, in 16-token tiles
+constexpr int MAX_B = ATTN_MAX_B;       // requests per call on the bf16 path (prefix kept in LDS)
+constexpr int ITEM_COST = ATTN_ITEM_COST;  // start-up cost of a piece, in 16-token tiles
 
 __device__ __forceinline__ int units_of(int L) { return (L + PAGE - 1) / PAGE + 1; }
 __device__ __forceinline__ int cost_of(int L) { return units_of(L) + ITEM_COST; }

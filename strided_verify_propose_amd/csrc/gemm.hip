@@ -20,7 +20,7 @@
 namespace isd {
 namespace {
 
-constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int BM = PROJ_BM, BN = PROJ_BN, BK = PROJ_BK;
 constexpr int THREADS = 256;
 constexpr int PROJ_RING = 4;  // register stages of the load pipeline
 constexpr int A_LOADS = BM * BK / 8 / THREADS;  // 16-byte loads per thread per k step
@@ -267,14 +267,6 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(const ProjLaunch p) {
 }
 
 }  // namespace
-
-int proj_ksplit(int M, int K, int Nout) {
-  // the base tiles alone (not the A^T columns) decide, so gated and base-only calls agree
-  const int tiles = ((M + BM - 1) / BM) * (Nout / BN);
-  int s = 1;
-  while (s < 8 && tiles * s * 2 <= 256 && (K / (2 * s)) % BK == 0 && K / (2 * s) >= 4 * BK) s *= 2;
-  return s;
-}
 
 hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s) {
   const long long n = (long long)p.M * ((p.Nout + p.r) / 4);

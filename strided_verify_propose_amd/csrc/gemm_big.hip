@@ -35,8 +35,8 @@ namespace {
 
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
-constexpr int TBM = 224;                       // rows per workgroup
-constexpr int TBN = 256;                       // stacked weight rows (output columns) per workgroup
+constexpr int TBM = PROJ_BIG_TBM;              // rows per workgroup
+constexpr int TBN = PROJ_BIG_TBN;              // stacked weight rows (output columns) per workgroup
 constexpr int WM = TBM / 2;                    // 112 rows per wave (waves 2 in M x 4 in N)
 constexpr int WN = TBN / 4;                    // 64 columns per wave
 constexpr int RB = WM / 16;                    // 7 row blocks per wave
@@ -48,12 +48,6 @@ constexpr int LPW = (NF + WAVES - 1) / WAVES;  // loads per wave per step: 4 (wa
 constexpr int RING = 4;                        // LDS slots: RING - 1 k steps of loads in flight
 constexpr int SLOT = NF * 1024;                // bytes per slot
 constexpr int PFRAG = 64 * 8;                  // elements of one packed fragment
-// When the path is taken (measured against the 64 x 128 kernels, gated calls at M = 448:
-// K = 12288 71 vs 83 us, Nout = 12288 82 vs 84 us; M = 1344: 82 vs 91 us; but K = Nout =
-// 4096 42 vs 36 us, since 18 k steps per range do not pay for the partials' write and read):
-constexpr int MIN_ROWS = 192;                  // a 224-row tile at least 6/7 used
-constexpr int MIN_STEPS = 48;                  // k steps per range
-constexpr int MIN_GRID = 192;                  // workgroups: three quarters of the CUs or more
 
 template <bool PACKED>
 __global__ __launch_bounds__(THREADS, 1) void base_big_kernel(const ProjLaunch p) {
@@ -172,13 +166,6 @@ __global__ __launch_bounds__(THREADS, 1) void base_big_kernel(const ProjLaunch p
 }
 
 }  // namespace
-
-int proj_big_split(int M, int K, int Nout) {
-  // tiles counted with room for a rank-128 A^T, so the gated and the base-only call agree
-  const int mt = (M + TBM - 1) / TBM, nt = (Nout + 128 + TBN - 1) / TBN;
-  const int s = std::min(256 / (mt * nt), (K / 32) / MIN_STEPS);
-  return (M >= MIN_ROWS && s >= 2 && mt * nt * s >= MIN_GRID) ? s : 0;
-}
 
 hipError_t launch_proj_big(const ProjLaunch& p, bool packed, hipStream_t s) {
   const int mt = (p.M + TBM - 1) / TBM, nt = (p.Nout + p.r + TBN - 1) / TBN;

@@ -24,7 +24,7 @@
 namespace isd {
 namespace {
 
-constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int BM = PROJ_BM, BN = PROJ_BN, BK = PROJ_BK;
 constexpr int RING = 4;                         // register stages of the load pipeline
 constexpr int FRAG = 64 * 8;                    // elements in one packed 16 x 32 fragment
 

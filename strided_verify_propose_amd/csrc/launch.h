@@ -1,137 +1,21 @@
 // Host-side launch interface between the C ABI (isd_api.cpp) and the kernels (*.hip).
-// Arguments have already been validated when these are called.
+// Arguments have already been validated (isd_validate.cpp) when these are called.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include "launch_types.h"
+
 namespace isd {
 
-// ---------------------------------------------------------------- attention
-struct AttnLaunch {
-  int dtype;  // 0 f32, 1 bf16
-  const void* q;
-  const void* k_new;
-  const void* v_new;
-  void* k_cache;
-  void* v_cache;
-  const int32_t* page_table;
-  const int32_t* ctx_lens;
-  void* out;
-  int B, N, R, Hq, Hkv, G, D;
-  int max_pages;
-  int num_pages;
-  int max_ctx_len;
-  float scale;
-  // workspace carve-up: two partial slots per workgroup of the balanced grid
-  float* part_o;         // [ATTN_MAX_WG * 2][R*G][D]
-  float* part_ml;        // [ATTN_MAX_WG * 2][R*G][2]
-};
-constexpr int ATTN_MAX_WG = 2048;  // workgroups of the balanced attention grid, at most
-constexpr int ATTN_MAX_B = 2048;   // requests per bf16 attention call
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
-
-// ---------------------------------------------------------------- verification
-constexpr int VCHUNK = 16384;   // vocab entries per stats workgroup
-constexpr int VSUB = 1024;      // vocab entries per sub-chunk (prefix granularity)
-constexpr int VCHUNK_SUBS = VCHUNK / VSUB;
-
-struct WalkState {              // per request, written by the walk, read by the residual pass
-  int rej;                      // first rejected draft index, -1 if none / handled in the walk
-  int pad;
-  double up;                    // (u - a) / (1 - a)
-  double zp;                    // Z of p_{rej} (units of 2^(l c2 - kp))
-  float kp, kq;                 // row references (max of the chunk references) of p_{rej}, q~_{rej}
-  float izp_hi, izp_lo;         // 1/Z of p_{rej}, split hi + lo
-  float izq_hi, izq_lo;
-};
-
-struct VerifyLaunch {
-  int dtype;
-  const void* logits;
-  const void* draft;            // may be null
-  const int32_t* draft_ids;
-  const float* u;
-  int B, N, R, RR, V, SV, NSUB;
-  int srow0, snrow;             // rows srow0 .. srow0 + snrow - 1 of each request get the stats pass
-  float invT, c2;               // 1/T and log2(e)/T
-  int32_t* n_accept;
-  uint8_t* accept;
-  int32_t* next_token;
-  int32_t* argmax_ids;
-  int32_t* sampled_ids;
-  float* p_draft;
-  float* q_draft;
-  float* row_lse;
-  // workspace
-  float* cmax;                  // [B][RR][SV]  chunk max of raw logits
-  float* cref;                  // [B][RR][SV]  chunk reference K = fp32(cmax * c2)
-  int32_t* cidx;                // [B][RR][SV]  lowest index of the chunk max
-  float* csub;                  // [B][RR][NSUB] sum 2^(l c2 - K) per sub-chunk
-  WalkState* ws;                // [B]
-  float* rsub;                  // [B][NSUB] residual mass per sub-chunk
-};
 hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);        // stats + tail
 hipError_t launch_verify_stats(const VerifyLaunch& v, hipStream_t s);  // the stats pass alone
 hipError_t launch_verify_tail(const VerifyLaunch& v, hipStream_t s);   // walk, residual, draws
-
-// ---------------------------------------------------------------- LM head
-constexpr int LMH_MINI = 128;   // vocabulary columns per mini-chunk record of the LM head
-
-struct LmhLaunch {
-  const uint16_t* hidden;       // [M, Dm] bf16, row b R + r
-  const uint16_t* w;            // [V, Dm] bf16
-  uint16_t* logits;             // [M, V] bf16 out
-  int M, Dm, V, NMINI;          // NMINI = ceil(V / LMH_MINI)
-  int NMS;                      // row stride of the mini-chunk records: NMINI rounded up to 8
-  float c2;                     // log2(e)/T
-  float* mmax;                  // [M][NMS] mini-chunk max; null: logits only
-  float* msum;                  // [M][NMS] sum 2^(l c2 - fp32(max c2))
-  int32_t* marg;                // [M][NMS] lowest column holding the max
-  // merge into the verification's records (rows b RR + r, r < R)
-  int N, R, RR, SV, NSUB;
-  float* cmax;
-  float* cref;
-  int32_t* cidx;
-  float* csub;
-};
 hipError_t launch_lm_head(const LmhLaunch& p, hipStream_t s);        // logits (+ mini-chunk records)
 hipError_t launch_lm_head_merge(const LmhLaunch& p, hipStream_t s);  // records -> chunk records
-
-// ---------------------------------------------------------------- commit
-struct CommitLaunch {
-  const int32_t* n_accept;      // [B]
-  const int32_t* next_token;    // [B]
-  const int32_t* sampled_ids;   // [B][N]
-  int32_t* draft_ids;           // [B][N-1] in: this step's drafts; out: the next step's
-  int32_t* ctx_lens;            // [B] in/out
-  int32_t* tokens;              // [B][N] committed tokens, -1 padded; may be null
-  int32_t* counts;              // [B] number committed; may be null
-  int B, N;
-};
 hipError_t launch_commit(const CommitLaunch& c, hipStream_t s);
-
-// ---------------------------------------------------------------- gated projection
-struct ProjLaunch {
-  const uint16_t* X;            // [M, K]
-  const uint16_t* W;            // [Nout, K]  (W^T)
-  const uint16_t* A;            // [r, K]     (A^T), null when ungated
-  const uint16_t* Bl;           // [Nout, r]  (B^T), null when ungated
-  const uint8_t* gate;          // [M] or null (base only)
-  uint16_t* Y;                  // [M, Nout] bf16
-  int M, K, Nout, r;            // r = 0 when ungated
-  float* Ybase;                 // workspace [M, Nout] fp32 (rows with gate 1)
-  uint16_t* T;                  // workspace [M, r] bf16
-  const uint16_t* Sp;           // packed path: [W^T; A^T] in fragment order
-  int ksplit;                   // K split into this many equal parts (1: none)
-  float* part;                  // workspace [ksplit][M][Nout + r] fp32 partial sums (ksplit > 1)
-  int big;                      // 224 x 256 tiles over ksplit ranges of whole k steps
-};
-// K split of the projection for few tiles: a function of (M, K, Nout) only, so that a
-// gated call and the base-only call on the same x, w split -- and round -- alike.
-int proj_ksplit(int M, int K, int Nout);
-// K ranges of the large-tile path, or 0 when the 64 x 128 kernels serve (M, K, Nout).
-int proj_big_split(int M, int K, int Nout);
 // Large-tile partial sums, their ordered sum, and the delta on gated rows.
 hipError_t launch_proj_big(const ProjLaunch& p, bool packed, hipStream_t s);
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s);

@@ -111,9 +111,11 @@ _ws_cache: dict = {}
 
 
 def workspace(kind: str, nbytes: int, device, shape_key=()) -> torch.Tensor:
-    """Device workspace, one per (entry point, device, shape arguments), kept for reuse.
-    The library does not depend on its contents on entry."""
-    key = (kind, str(device), tuple(shape_key))
+    """Device workspace, one per (entry point, device, current stream, shape arguments),
+    kept for reuse: calls on different streams never share one, since calls that share a
+    workspace must not overlap.  The library does not depend on its contents on entry."""
+    stream = torch.cuda.current_stream(device).cuda_stream
+    key = (kind, str(device), stream, tuple(shape_key))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -149,6 +151,8 @@ def attention_step(q, k_new, v_new, k_cache, v_cache, page_table, ctx_lens, max_
     _need(k_cache, "k_cache", q.dtype, (P, Hkv, D // 8, PAGE_SIZE, 8), dev)
     _need(v_cache, "v_cache", q.dtype, (P, Hkv, D // 16, 4, PAGE_SIZE, 4), dev)
     _need(page_table, "page_table", torch.int32, device=dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError(f"page_table: shape {tuple(page_table.shape)}, expected ({B}, max_pages)")
     _need(ctx_lens, "ctx_lens", torch.int32, (B,), dev)
     if out is None:
         out = torch.empty_like(q)

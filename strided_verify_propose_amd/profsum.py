@@ -7,7 +7,7 @@
 The HBM summary scales each kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a 1 GiB device-to-device copy in the same run, and
 records the SHA-256 of the attention sources it was taken on (attention.hip, device.h and
-the attention section of launch.h), so that a reader can tell when the counters no longer
+the attention section of launch_types.h), so that a reader can tell when the counters no longer
 describe the kernel.
 """
 from __future__ import annotations
@@ -19,9 +19,9 @@ import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-ATTN_SOURCES = ["csrc/attention.hip", "csrc/device.h", "csrc/launch.h"]
-# in launch.h only the attention section (up to the next section rule) feeds the kernel
-SECTION_OF = {"csrc/launch.h": "// ---------------------------------------------------------------- attention"}
+ATTN_SOURCES = ["csrc/attention.hip", "csrc/device.h", "csrc/launch_types.h"]
+# in launch_types.h only the attention section (up to the next section rule) feeds the kernel
+SECTION_OF = {"csrc/launch_types.h": "// ---------------------------------------------------------------- attention"}
 SECTION_RULE = "// ----------------------------------------------------------------"
 COPY_BYTES = 1 << 30
 

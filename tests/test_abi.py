@@ -66,6 +66,9 @@ def att(L, **kw):
     (dict(wsb=100, maxctx=3000, maxp=200), WORKSPACE),   # long enough to need splits
     (dict(ws=None, maxctx=3000, maxp=200), WORKSPACE),
     (dict(dt=0, maxctx=20000, maxp=2000), UNSUPPORTED),  # f32 path token limit
+    # 2048 requests x 8 KV heads at 2.2M tokens: the work list's 32-bit cost sum would overflow
+    (dict(B=2048, maxctx=2200000, maxp=137502), UNSUPPORTED),
+    (dict(Hq=65536 * 8), INVALID),
 ])
 def test_attention_validation(L, kw, status):
     assert att(L, **kw) == status

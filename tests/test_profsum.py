@@ -24,7 +24,7 @@ def test_hash_tracks_attention_code_only(tmp_path, monkeypatch):
     _copy_sources(tmp_path)
     monkeypatch.setattr(profsum, "ROOT", str(tmp_path))
     h0 = profsum.attention_source_hash()
-    launch = tmp_path / "csrc" / "launch.h"
+    launch = tmp_path / "csrc" / "launch_types.h"
     # another kernel's section of the header: ignored
     _edit(launch, "int M, Dm, V, NMINI;", "int M, Dm, V, NMINI, EXTRA;")
     assert profsum.attention_source_hash() == h0
