@@ -145,6 +145,27 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
                       float* p_draft, float* q_draft, float* row_lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- verification, no workspace
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  isd_verify with the same arguments
+ * and results, minus the workspace: its scratch space is a fixed device array of
+ * ISD_VERIFY_NOALLOC_MAX_BYTES that the library holds on every GPU it runs on until the
+ * process ends.  Nothing is allocated; the first call on a device (with that device
+ * current) looks up the array's address there.
+ *   - A shape whose isd_verify_workspace_bytes exceeds ISD_VERIFY_NOALLOC_MAX_BYTES returns
+ *     ISD_ERR_UNSUPPORTED (B=64, N=4, V=151936 needs about 0.5 MB; the array holds about
+ *     1300 such requests).  Every other check and error is isd_verify's.
+ *   - Every call on a GPU uses that GPU's one array, which keeps the last call's contents
+ *     (nothing in it needs to start at zero).  Calls that overlap on one GPU -- on
+ *     concurrent streams or from several threads -- race on it: serialise them.
+ *   - `stream` must belong to the current device. */
+#define ISD_VERIFY_NOALLOC_MAX_BYTES (8u << 20)
+isd_status isd_verify_noalloc(isd_dtype dt, const void* logits, const void* draft_logits,
+                              const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                              float temperature, int32_t* n_accept, uint8_t* accept,
+                              int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                              float* p_draft, float* q_draft, float* row_lse, void* stream);
+
 /* ---------------------------------------------------------------- commit
  * What one step keeps, per request -- the two-state chain of tokens per forward
  * (「I-DLM – introspektive Diffusion Language Models」 "Speedup Factor Explorer"; the step

@@ -15,7 +15,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attention.hip", "verify.hip", "commit.hip", "gemm.hip", "gemm_packed.hip", "gemm_big.hip",
            "lm_head.hip",
-           "isd_validate.cpp", "isd_api.cpp"]
+           "scratch.hip", "isd_validate.cpp", "isd_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
-           "isd_verify_workspace_bytes", "isd_verify",
+           "isd_verify_workspace_bytes", "isd_verify", "isd_verify_noalloc",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
            "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed",
            "isd_commit", "isd_lm_head", "isd_lm_head_verify_workspace_bytes",
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L.isd_verify_workspace_bytes.argtypes = [i32] * 3
     L.isd_verify.restype = i32
     L.isd_verify.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 8 + [vp, sz, vp]
+    L.isd_verify_noalloc.restype = i32
+    L.isd_verify_noalloc.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 8 + [vp]
     L.isd_gated_lora_workspace_bytes.restype = sz
     L.isd_gated_lora_workspace_bytes.argtypes = [i32] * 4
     L.isd_gated_lora_proj.restype = i32
@@ -204,6 +206,37 @@ def verify(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
                         _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
                         _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
                         _ptr(out.get("row_lse")), _ptr(w), w.numel(), _stream(dev)))
+    return out
+
+
+def verify_noalloc(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
+                   out: dict | None = None):
+    """verify() without a workspace (isd_verify_noalloc): the library's fixed scratch array
+    on the current device serves instead, so the call allocates nothing when `out` is
+    given.  Calls that overlap on one GPU race on that array.  Returns verify()'s dict."""
+    B, R, V = logits.shape
+    if R % 2 == 0:
+        raise ValueError("logits must hold 2N-1 rows per request")
+    N = (R + 1) // 2
+    dev = logits.device
+    _need(logits, "logits", logits.dtype, device=dev)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", logits.dtype, (B, N - 1, V), dev)
+    _need(draft_ids, "draft_ids", torch.int32, (B, N - 1), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, R), dev)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(n_accept=torch.empty(B, **i32),
+                   accept=torch.empty((B, N - 1), dtype=torch.uint8, device=dev),
+                   next_token=torch.empty(B, **i32), argmax_ids=torch.empty((B, N), **i32),
+                   sampled_ids=torch.empty((B, N), **i32), p_draft=torch.empty((B, N - 1), **f32),
+                   q_draft=torch.empty((B, N - 1), **f32), row_lse=torch.empty((B, R + N - 1), **f32))
+    _check(lib().isd_verify_noalloc(_dt(logits), _ptr(logits), _ptr(draft_logits), _ptr(draft_ids),
+                                    _ptr(uniforms), B, N, V, float(temperature), _ptr(out["n_accept"]),
+                                    _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
+                                    _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")),
+                                    _ptr(out.get("q_draft")), _ptr(out.get("row_lse")), _stream(dev)))
     return out
 
 
