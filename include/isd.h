@@ -104,6 +104,21 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
                               int max_ctx_len, float scale, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- page layout conversion
+ * The paged KV cache as the pages state it -- a page table over fixed pages of 16 token
+ * slots, each slot one row of D values per KV head (「首次超越 AR 模型」 "實際部署：SGLang 整合",
+ * paged KV cache) -- converted to and from the tile layout isd_attention_step reads.
+ *   k_pages, v_pages   [num_pages, Hkv, 16, D]: element (page p, head h, slot t, dim d)
+ *                      at ((p*Hkv + h)*16 + t)*D + d
+ *   k_cache, v_cache   the tile layouts documented at isd_attention_step
+ * isd_pack_kv_pages writes k_cache / v_cache from k_pages / v_pages; isd_unpack_kv_pages
+ * does the reverse.  Bit copies of every element, asynchronous on `stream`; source and
+ * destination must not overlap.  dtype ISD_BF16 or ISD_F32; D in {64, 128}. */
+isd_status isd_pack_kv_pages(isd_dtype dt, const void* k_pages, const void* v_pages, void* k_cache,
+                             void* v_cache, int num_pages, int Hkv, int D, void* stream);
+isd_status isd_unpack_kv_pages(isd_dtype dt, const void* k_cache, const void* v_cache, void* k_pages,
+                               void* v_pages, int num_pages, int Hkv, int D, void* stream);
+
 /* ---------------------------------------------------------------- verification
  * Vocab-wide verification of one ISD step.  Follows: proposals at [MASK] positions from
  * q and verification at clean positions against the anchor p with acceptance

@@ -54,6 +54,22 @@ isd_status isd_attention_step(isd_dtype dt, const void* q, const void* k_new, co
   return hip_status(isd::launch_attention(a, as_stream(stream)), "attention launch");
 }
 
+isd_status isd_pack_kv_pages(isd_dtype dt, const void* k_pages, const void* v_pages, void* k_cache,
+                             void* v_cache, int num_pages, int Hkv, int D, void* stream) {
+  isd::KvPagesLaunch c;
+  const isd_status st = isd::prepare_kv_pages(dt, k_pages, v_pages, k_cache, v_cache, num_pages, Hkv, D, 1, &c);
+  if (st != ISD_OK) return st;
+  return hip_status(isd::launch_kv_pages(c, as_stream(stream)), "pack_kv_pages launch");
+}
+
+isd_status isd_unpack_kv_pages(isd_dtype dt, const void* k_cache, const void* v_cache, void* k_pages,
+                               void* v_pages, int num_pages, int Hkv, int D, void* stream) {
+  isd::KvPagesLaunch c;
+  const isd_status st = isd::prepare_kv_pages(dt, k_cache, v_cache, k_pages, v_pages, num_pages, Hkv, D, 0, &c);
+  if (st != ISD_OK) return st;
+  return hip_status(isd::launch_kv_pages(c, as_stream(stream)), "unpack_kv_pages launch");
+}
+
 // ---------------------------------------------------------------- verification
 size_t isd_verify_workspace_bytes(int B, int N, int V) { return isd::verify_workspace_bytes(B, N, V); }
 

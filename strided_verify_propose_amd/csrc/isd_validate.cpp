@@ -262,6 +262,28 @@ isd_status prepare_attention(isd_dtype dt, const void* q, const void* k_new, con
   return clear_error();
 }
 
+// ---------------------------------------------------------------- page layout conversion
+isd_status prepare_kv_pages(isd_dtype dt, const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                            int num_pages, int Hkv, int D, int to_tiles, KvPagesLaunch* c) {
+  const char* who = to_tiles ? "pack_kv_pages" : "unpack_kv_pages";
+  if (dt != ISD_F32 && dt != ISD_BF16) return set_error(ISD_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dt);
+  if (!k_src || !v_src || !k_dst || !v_dst) return set_error(ISD_ERR_INVALID_ARG, "%s: null tensor pointer", who);
+  if (num_pages < 1 || Hkv < 1 || Hkv > 65535)
+    return set_error(ISD_ERR_INVALID_ARG, "%s: num_pages=%d Hkv=%d", who, num_pages, Hkv);
+  if (D != 64 && D != 128) return set_error(ISD_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", who, D);
+  if ((long long)num_pages * Hkv * ATTN_PAGE * D > (1LL << 40))
+    return set_error(ISD_ERR_UNSUPPORTED, "%s: %d pages x %d heads exceed 2^40 elements per call", who, num_pages,
+                     Hkv);
+  if (k_src == k_dst || v_src == v_dst || k_src == v_dst || v_src == k_dst)
+    return set_error(ISD_ERR_INVALID_ARG, "%s: source and destination must not overlap", who);
+  *c = KvPagesLaunch{};
+  c->dtype = dt == ISD_BF16 ? 1 : 0;
+  c->to_tiles = to_tiles ? 1 : 0;
+  c->k_src = k_src; c->v_src = v_src; c->k_dst = k_dst; c->v_dst = v_dst;
+  c->num_pages = num_pages; c->Hkv = Hkv; c->D = D;
+  return clear_error();
+}
+
 // ---------------------------------------------------------------- verification
 isd_status prepare_verify(isd_dtype dt, const void* logits, const void* draft_logits,
                           const int32_t* draft_ids, const float* uniforms, int B, int N, int V,

@@ -34,6 +34,17 @@ constexpr int ATTN_PAGE = 16;      // tokens per page
 // the requests of a call is kept in 32-bit integers.
 constexpr int ATTN_ITEM_COST = 24;
 
+// Conversion between logical pages [num_pages][Hkv][16][D] and the attention tile layout.
+struct KvPagesLaunch {
+  int dtype;             // 0 f32, 1 bf16
+  int to_tiles;          // 1: logical -> tiles, 0: tiles -> logical
+  const void* k_src;
+  const void* v_src;
+  void* k_dst;
+  void* v_dst;
+  int num_pages, Hkv, D;
+};
+
 // ---------------------------------------------------------------- verification
 constexpr int VCHUNK = 16384;   // vocab entries per stats workgroup
 constexpr int VSUB = 1024;      // vocab entries per sub-chunk (prefix granularity)

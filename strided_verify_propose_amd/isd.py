@@ -23,6 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
+           "isd_pack_kv_pages", "isd_unpack_kv_pages",
            "isd_verify_workspace_bytes", "isd_verify", "isd_verify_noalloc",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
            "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed",
@@ -53,6 +54,10 @@ def lib() -> ctypes.CDLL:
     L.isd_attention_workspace_bytes.argtypes = [i32] * 6
     L.isd_attention_step.restype = i32
     L.isd_attention_step.argtypes = [i32] + [vp] * 8 + [i32] * 9 + [f32, vp, sz, vp]
+    L.isd_pack_kv_pages.restype = i32
+    L.isd_pack_kv_pages.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [vp]
+    L.isd_unpack_kv_pages.restype = i32
+    L.isd_unpack_kv_pages.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [vp]
     L.isd_verify_workspace_bytes.restype = sz
     L.isd_verify_workspace_bytes.argtypes = [i32] * 3
     L.isd_verify.restype = i32
@@ -169,6 +174,42 @@ def attention_step(q, k_new, v_new, k_cache, v_cache, page_table, ctx_lens, max_
                                 B, N, Hq, Hkv, D, PAGE_SIZE, page_table.shape[1], P,
                                 int(max_ctx_len), float(scale), _ptr(w), w.numel(), _stream(dev)))
     return out
+
+
+def pack_kv_pages(k_pages, v_pages, k_cache=None, v_cache=None):
+    """Logical pages k_pages, v_pages [P, Hkv, 16, D] -> the tile layout attention_step reads
+    (k_cache [P, Hkv, D/8, 16, 8], v_cache [P, Hkv, D/16, 4, 16, 4]).  Returns (k_cache, v_cache)."""
+    P, Hkv, T, D = k_pages.shape
+    dev = k_pages.device
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        _need(t, name, k_pages.dtype, (P, Hkv, PAGE_SIZE, D), dev)
+    if k_cache is None:
+        k_cache = torch.empty((P, Hkv, D // 8, PAGE_SIZE, 8), dtype=k_pages.dtype, device=dev)
+    if v_cache is None:
+        v_cache = torch.empty((P, Hkv, D // 16, 4, PAGE_SIZE, 4), dtype=k_pages.dtype, device=dev)
+    _need(k_cache, "k_cache", k_pages.dtype, (P, Hkv, D // 8, PAGE_SIZE, 8), dev)
+    _need(v_cache, "v_cache", k_pages.dtype, (P, Hkv, D // 16, 4, PAGE_SIZE, 4), dev)
+    _check(lib().isd_pack_kv_pages(_dt(k_pages), _ptr(k_pages), _ptr(v_pages), _ptr(k_cache), _ptr(v_cache),
+                                   P, Hkv, D, _stream(dev)))
+    return k_cache, v_cache
+
+
+def unpack_kv_pages(k_cache, v_cache, k_pages=None, v_pages=None):
+    """The tile layout back to logical pages [P, Hkv, 16, D].  Returns (k_pages, v_pages)."""
+    P, Hkv = k_cache.shape[:2]
+    D = k_cache.shape[2] * 8
+    dev = k_cache.device
+    _need(k_cache, "k_cache", k_cache.dtype, (P, Hkv, D // 8, PAGE_SIZE, 8), dev)
+    _need(v_cache, "v_cache", k_cache.dtype, (P, Hkv, D // 16, 4, PAGE_SIZE, 4), dev)
+    if k_pages is None:
+        k_pages = torch.empty((P, Hkv, PAGE_SIZE, D), dtype=k_cache.dtype, device=dev)
+    if v_pages is None:
+        v_pages = torch.empty((P, Hkv, PAGE_SIZE, D), dtype=k_cache.dtype, device=dev)
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        _need(t, name, k_cache.dtype, (P, Hkv, PAGE_SIZE, D), dev)
+    _check(lib().isd_unpack_kv_pages(_dt(k_cache), _ptr(k_cache), _ptr(v_cache), _ptr(k_pages), _ptr(v_pages),
+                                     P, Hkv, D, _stream(dev)))
+    return k_pages, v_pages
 
 
 # ----------------------------------------------------------------------------- verification

@@ -32,6 +32,10 @@ int main(void) {
   CHECK(isd_commit(fake, fake, fake, fake, fake, NULL, NULL, 4, 9, NULL) == ISD_ERR_UNSUPPORTED);
   CHECK(isd_gated_lora_proj(fake, fake, fake, fake, fake, fake, 0, 4096, 4096, 128, fake, 1 << 30,
                             NULL) == ISD_ERR_INVALID_ARG);
+  CHECK(isd_pack_kv_pages(ISD_BF16, fake, (void*)0x2000, (void*)0x3000, (void*)0x4000, 10, 8, 96, NULL) ==
+        ISD_ERR_UNSUPPORTED);
+  CHECK(isd_unpack_kv_pages(ISD_BF16, NULL, fake, (void*)0x3000, (void*)0x4000, 10, 8, 128, NULL) ==
+        ISD_ERR_INVALID_ARG);
   if (fails == 0) printf("c abi ok\n");
   return fails == 0 ? 0 : 1;
 }

@@ -74,6 +74,20 @@ static void attention_cases() {
   CHECK(a.dtype == 0 && a.part_o == nullptr);
 }
 
+static void kv_pages_cases() {
+  KvPagesLaunch c{};
+  void* k = reinterpret_cast<void*>(0x1000);
+  void* v = reinterpret_cast<void*>(0x2000);
+  void* kc = reinterpret_cast<void*>(0x3000);
+  void* vc = reinterpret_cast<void*>(0x4000);
+  CHECK(prepare_kv_pages(ISD_BF16, k, v, kc, vc, 1000, 8, 128, 1, &c) == ISD_OK && c.to_tiles == 1);
+  CHECK(prepare_kv_pages(ISD_F32, kc, vc, k, v, 1000, 8, 64, 0, &c) == ISD_OK && c.to_tiles == 0 && c.dtype == 0);
+  CHECK(prepare_kv_pages(ISD_BF16, k, v, k, vc, 1000, 8, 128, 1, &c) == ISD_ERR_INVALID_ARG);
+  CHECK(prepare_kv_pages(ISD_BF16, k, v, kc, vc, 1000, 8, 80, 1, &c) == ISD_ERR_UNSUPPORTED);
+  CHECK(prepare_kv_pages(ISD_BF16, k, v, kc, vc, INT_MAX, 65535, 128, 1, &c) == ISD_ERR_UNSUPPORTED);
+  CHECK(prepare_kv_pages(ISD_BF16, k, nullptr, kc, vc, 10, 8, 128, 1, &c) == ISD_ERR_INVALID_ARG);
+}
+
 static void verify_cases() {
   const size_t need = verify_workspace_bytes(64, 4, 151936);
   char* base = reinterpret_cast<char*>(0x4000000);
@@ -179,6 +193,11 @@ static void fuzz(int iters) {
       if (st == ISD_OK && a.part_o) CHECK(need > 0 && inside(a.part_ml, 8, base, need));
     }
     {
+      KvPagesLaunch c{};
+      (void)prepare_kv_pages(ISD_BF16, P, reinterpret_cast<void*>(0x200000), reinterpret_cast<void*>(0x300000),
+                             reinterpret_cast<void*>(0x400000), a0, a1, a2, it & 1, &c);
+    }
+    {
       const size_t need = verify_workspace_bytes(a0, a1, a2);
       VerifyLaunch v{};
       const isd_status st = prepare_verify(ISD_BF16, P, it % 3 ? P : nullptr, (const int32_t*)P, (const float*)P, a0,
@@ -216,6 +235,7 @@ static void fuzz(int iters) {
 
 int main() {
   attention_cases();
+  kv_pages_cases();
   verify_cases();
   proj_and_lm_head_cases();
   fuzz(200000);

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -234,3 +234,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(isd, "_LIB_PATH", str(tmp_path / "libisd.so"))
     with pytest.raises(RuntimeError, match="is not built"):
         isd.lib()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((7, FAKE, FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 10, 8, 128), INVALID),
+    ((1, None, FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 10, 8, 128), INVALID),
+    ((1, FAKE, ctypes.c_void_p(0x1800), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 0, 8, 128), INVALID),
+    ((1, FAKE, ctypes.c_void_p(0x1800), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 10, 8, 96), UNSUPPORTED),
+    ((1, FAKE, ctypes.c_void_p(0x1800), FAKE, ctypes.c_void_p(0x3000), 10, 8, 128), INVALID),   # overlap
+    ((1, FAKE, ctypes.c_void_p(0x1800), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 1 << 30, 65535, 128),
+     UNSUPPORTED),
+])
+def test_kv_pages_validation(L, args, status):
+    assert L.isd_pack_kv_pages(*args, None) == status
+    assert L.isd_unpack_kv_pages(*args, None) == status
+    assert L.isd_last_error() != b""

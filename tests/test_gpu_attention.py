@@ -96,3 +96,96 @@ def test_most_requests_per_call():
     ctx = list(np.random.default_rng(5).integers(0, 41, 2048))
     run(step_cfg("max_b", "bf16", 2048, 2, 8, 2, 64, 301), ctx_lens=ctx,
         sample=[0, 1, 700, 1023, 1024, 2047])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_pack_kv_pages_is_the_tile_layout_and_round_trips(dtype, D):
+    """isd_pack_kv_pages gives exactly the documented tile layout of logical pages, and
+    isd_unpack_kv_pages gives them back, bit for bit."""
+    cfg = step_cfg("pack_pages", dtype, 3, 4, 8, 2, D, 131)
+    inp = synth.attention_inputs(cfg, ctx_lens=[5, 40, 300])
+    print(f"pack_kv_pages {dtype} D={D} pages={inp.num_pages}", flush=True)
+    kc, vc = isd.pack_kv_pages(to_dev(inp.k_pages), to_dev(inp.v_pages))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(kc), synth.k_tile_layout(inp.k_pages))
+    assert np.array_equal(to_np(vc), synth.v_tile_layout(inp.v_pages))
+    kp, vp = isd.unpack_kv_pages(kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(kp), inp.k_pages)
+    assert np.array_equal(to_np(vp), inp.v_pages)
+
+
+def test_plain_c_step_from_logical_pages(tmp_path):
+    """A C program using only include/isd.h and the HIP runtime packs logical pages,
+    runs the step and unpacks the cache; the output matches the oracle and the cache
+    after the step is the oracle's append, bit for bit."""
+    import os
+    import shutil
+    import subprocess
+    from tests.test_abi_c import ROOT
+    from strided_verify_propose_amd.build import LIB
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "step_from_pages"
+    libdir = os.path.dirname(LIB)
+    subprocess.run([gcc, "-std=c99", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", os.path.join(ROOT, "tests", "c", "step_from_pages.c"), "-o", str(exe),
+                    "-L", libdir, "-lisd", f"-Wl,-rpath,{libdir}", "-L", "/opt/rocm/lib", "-lamdhip64",
+                    "-Wl,-rpath,/opt/rocm/lib", "-lm"], check=True)
+    cfg = step_cfg("c_pages", "bf16", 4, 4, 32, 8, 128, 141)
+    inp = synth.attention_inputs(cfg, ctx_lens=[0, 17, 513, 1100])
+    print(f"c caller step B={cfg.B} ctx={inp.ctx_lens.tolist()} pages={inp.num_pages}", flush=True)
+    hdr = np.array([cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, inp.num_pages, inp.page_table.shape[1],
+                    int(inp.ctx_lens.max())], np.int32)
+    src = tmp_path / "in.bin"
+    with open(src, "wb") as f:
+        for a in (hdr, inp.q, inp.k_new, inp.v_new, inp.k_pages, inp.v_pages,
+                  inp.page_table.astype(np.int32), inp.ctx_lens.astype(np.int32)):
+            f.write(np.ascontiguousarray(a).tobytes())
+    dst = tmp_path / "out.bin"
+    res = subprocess.run([str(exe), str(src), str(dst)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    raw = np.fromfile(dst, np.uint16)
+    nq, npg = inp.q.size, inp.k_pages.size
+    out = raw[:nq].reshape(inp.q.shape)
+    kp = raw[nq:nq + npg].reshape(inp.k_pages.shape)
+    vp = raw[nq + npg:].reshape(inp.v_pages.shape)
+    ref, rkp, rvp = oracle.attention_step(inp.q, inp.k_new, inp.v_new, inp.k_pages, inp.v_pages,
+                                          inp.page_table, inp.ctx_lens, inp.scale)
+    assert np.array_equal(kp, rkp) and np.array_equal(vp, rvp), "cache after the step"
+    assert_close(out, ref, RTOL["bf16"], "attention output from the C caller")
+
+
+def test_stale_slots_past_the_context_change_nothing():
+    """Rollback is not advancing ctx_lens: the slots of rejected drafts stay in the cache.
+    With those slots (and every other slot past each context, up to the end of its pages)
+    filled with garbage -- huge values and NaN bit patterns -- the step's output is
+    bitwise the output on a clean cache, and the block's append overwrites its slots."""
+    cfg = step_cfg("stale_slots", "bf16", 4, 4, 32, 8, 128, 151)
+    inp = synth.attention_inputs(cfg, ctx_lens=[3, 16, 37, 700])
+    print(f"stale slots ctx={inp.ctx_lens.tolist()}", flush=True)
+    dirty_k, dirty_v = inp.k_pages.copy(), inp.v_pages.copy()
+    rng = np.random.default_rng(7)
+    for b in range(cfg.B):
+        for j in range(int(inp.ctx_lens[b]), (int(inp.ctx_lens[b]) + cfg.R + 15) // 16 * 16):
+            p = inp.page_table[b, j // 16]
+            junk = rng.choice(np.array([0x7FC0, 0xFFC0, 0x7F7F, 0x4B00], np.uint16), size=(cfg.Hkv, cfg.D))
+            dirty_k[p, :, j % 16] = junk
+            dirty_v[p, :, j % 16] = junk[:, ::-1]
+    outs = []
+    for kp, vp in ((inp.k_pages, inp.v_pages), (dirty_k, dirty_v)):
+        d = device_inputs(inp)
+        d["k_cache"], d["v_cache"] = to_dev(synth.k_tile_layout(kp)), to_dev(synth.v_tile_layout(vp))
+        o = isd.attention_step(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["page_table"],
+                               d["ctx_lens"], int(inp.ctx_lens.max()))
+        torch.cuda.synchronize()
+        outs.append((to_np(o), synth.k_logical_layout(to_np(d["k_cache"]), cfg.D),
+                     synth.v_logical_layout(to_np(d["v_cache"]), cfg.D)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "stale slots changed the output"
+    for b in range(cfg.B):
+        for t in range(cfg.R):
+            j = int(inp.ctx_lens[b]) + t
+            p = inp.page_table[b, j // 16]
+            assert np.array_equal(outs[1][1][p, :, j % 16], inp.k_new[b, t])
+            assert np.array_equal(outs[1][2][p, :, j % 16], inp.v_new[b, t])
