@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="R-ISD decoder layer (Qwen3-8B shapes): gated against base-only time")
     ap.add_argument("--sweep-n", default="2,3,4")
+    ap.add_argument("--sweep-p", default="0.9,0.5",
+                    help="acceptance targets of the sweep (proposal noise bisected on the oracle)")
     ap.add_argument("--lm-head", action="store_true",
                     help="the LM head fused with verification (Qwen3-8B shapes) against the unfused pair")
     return ap.parse_args()
@@ -106,7 +108,6 @@ def main():
     from strided_verify_propose_amd.profsum import read_attention_traffic
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     def dt(a):
         a = np.ascontiguousarray(a)
@@ -119,18 +120,27 @@ def main():
     t0 = time.time()
     # ---- inputs (seeded, generated on the host once, then resident in HBM)
     att = synth.attention_inputs(scfg)
-    A = dict(q=dt(att.q), k_new=dt(att.k_new), v_new=dt(att.v_new),
-             k_cache=dt(synth.k_tile_layout(att.k_pages)), v_cache=dt(synth.v_tile_layout(att.v_pages)),
-             page_table=dt(att.page_table), ctx_lens=dt(att.ctx_lens))
     maxctx = int(att.ctx_lens.max())
     vsets = []
+    vsets_host = []
     ver0 = None
     for k in range(args.verify_sets):
         v = synth.verify_inputs(scfg, seed=scfg.seed + 100 * k)
         ver0 = v if ver0 is None else ver0
+        vsets_host.append(v)
+    pin = synth.proj_inputs(pcfg)
+    pool = None
+    if not args.no_cpu_baseline:
+        # worker processes for the all-core oracle baseline, forked now -- before anything
+        # touches the GPU -- so they inherit the host inputs and never share GPU state
+        pool = oracle_pool(att, ver0, pin, scfg)
+    torch.cuda.set_device(dev)
+    A = dict(q=dt(att.q), k_new=dt(att.k_new), v_new=dt(att.v_new),
+             k_cache=dt(synth.k_tile_layout(att.k_pages)), v_cache=dt(synth.v_tile_layout(att.v_pages)),
+             page_table=dt(att.page_table), ctx_lens=dt(att.ctx_lens))
+    for v in vsets_host:
         vsets.append(dict(logits=dt(v.logits), draft_logits=dt(v.draft_logits),
                           draft_ids=dt(v.draft_ids), uniforms=dt(v.uniforms)))
-    pin = synth.proj_inputs(pcfg)
     P = dict(x=dt(pin.x), w=dt(pin.w), a=dt(pin.a), b=dt(pin.b), gate=dt(pin.gate))
     # weights are packed once, outside the timed region, as a serving system would at load
     packed = None if args.proj_row_major else isd.pack_proj_weights(P["w"], P["a"], P["b"])
@@ -228,6 +238,11 @@ def main():
     p_flops = 2 * pcfg.M * pcfg.K * pcfg.Nout + 2 * m_g * pcfg.K * pcfg.r + 2 * m_g * pcfg.r * pcfg.Nout
     p_us = float(np.mean(proj_ms)) * 1e3
 
+    # the projection alone: back to back on one input set (weights warm in the last-level
+    # cache) and rotated over PROJ_SETS sets of activations and packed weights (cold), with
+    # hipBLASLt's time for the base product (torch.nn.functional.linear) as a reference
+    proj_alone = projection_alone(P, packed, pcfg, m_g, dev)
+
     # measured device copy ceiling: a 512 MiB device-to-device copy, timed with events
     src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -282,6 +297,7 @@ def main():
         "device_copy_GBps": round(copy_gbps, 1),
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
+        "proj_alone": proj_alone,
         "roofline": {"bound": "hbm",
                      "kernel": "isd_attention_step (attn_bf16_kernel + attn_combine_kernel)",
                      "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -291,18 +307,22 @@ def main():
         "eager_ms_per_step": round(1e3 * eager_s, 4),
         "input_generation_s": round(gen_s, 1),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(scfg, att, ver0, pin)
+    # the timed verification outputs against the oracle, draw by draw (the oracle runs on
+    # the host here; its time is not part of any figure)
+    line["verify_parity"] = verify_parity_counts(vsets_host, vouts, scfg.N)
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(scfg, att, ver0, pin, pool)
+        line["cpu_host"] = cpu_host_info(pool)
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 
 # ---------------------------------------------------------------- concurrency sweep
-SWEEP_SIGMA = 0.25  # proposal noise sd giving acceptance near 0.9 with anchor sd 3
-
-
 def sweep(args):
     """Steps/s and tokens/s of the whole step against the number of concurrent requests C
-    (one request = one 2N-1 row block), for each stride N: where the block stops being
+    (one request = one 2N-1 row block), for each stride N and acceptance target (0.9 and
+    0.5, the proposal noise calibrated on the oracle): where the block stops being
     memory-bound.  Qwen3-8B attention shapes with every context at 2048 tokens, the
     151936-entry vocabulary, the 4096 x 4096 r128 projection on C (2N-1) rows with the
     [MASK] rows gated.  Inputs are drawn on the device (torch generator seeded per point),
@@ -322,9 +342,12 @@ def sweep(args):
     b = (torch.randn((Nout, r), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
     packed = isd.pack_proj_weights(w, a, b)
     del w, a, b
+    from strided_verify_propose_amd import synth
     Cs = [int(c) for c in args.sweep_c.split(",")]
     Ns = [int(n) for n in args.sweep_n.split(",")]
-    for pi, (N, C) in enumerate([(n, c) for n in Ns for c in Cs]):
+    Ps = [float(p) for p in args.sweep_p.split(",")]
+    for pi, (p_target, N, C) in enumerate([(p, n, c) for p in Ps for n in Ns for c in Cs]):
+        sigma = synth.SWEEP_SIGMA[p_target]
         gen.manual_seed(1400 + pi)
         R = 2 * N - 1
         bf = torch.bfloat16
@@ -342,7 +365,7 @@ def sweep(args):
         vsets = []
         for _ in range(4):
             anchor = randn(C, R, V, sd=3.0)
-            prop = anchor + randn(C, R, V, sd=SWEEP_SIGMA)
+            prop = anchor + randn(C, R, V, sd=sigma)
             logits = torch.cat([anchor[:, :N - 1], prop[:, N - 1:]], dim=1).to(bf).contiguous()
             draft = prop[:, :N - 1].to(bf).contiguous()
             del anchor, prop
@@ -413,6 +436,7 @@ def sweep(args):
         p_flops = 2 * M * K * Nout + 2 * (C * N) * K * r + 2 * (C * N) * r * Nout
         print(json.dumps({
             "sweep": "concurrency", "stride_N": N, "C": C, "context": L, "query_rows": R,
+            "acceptance_target": p_target, "proposal_noise_sd": sigma,
             "ms_per_step": round(1e3 * el / steps, 4), "steps_per_s": round(sps, 1),
             "tokens_per_s": round(sps * C * tpf, 1), "p_hat": round(p_hat, 4),
             "tpf_closed_form_at_p_hat": round(tpf, 4),
@@ -630,34 +654,209 @@ def lm_head_bench(args):
         flush=True)
 
 
-def cpu_baseline(scfg, att, ver, pin, min_seconds=10.0):
-    """The oracle, as it is, on the host cores: whole steps of the same workload (the
-    projection, attention for all requests, verification for all requests, on the first
-    verification input set), repeated until about `min_seconds` of CPU work."""
-    from threadpoolctl import threadpool_info
+# ---------------------------------------------------------------- helpers of the main bench
+PROJ_SETS = 12   # rotated activation + weight sets for the cold projection timing
 
+
+def projection_alone(P, packed, pcfg, m_g, dev, reps=48):
+    """The R-ISD projection alone: back to back on one input set (the 43 MB of operands
+    stay in the 256 MB last-level cache: warm) and rotated over PROJ_SETS sets of
+    activations and packed weights (cold), HIP events around `reps` calls each.  The
+    base product through hipBLASLt (torch.nn.functional.linear, 448 x 4096 -> 4096, no
+    delta) is timed the same two ways as a reference."""
+    import torch
+
+    from strided_verify_propose_amd import isd
+    M, K, Nout, r = pcfg.M, pcfg.K, pcfg.Nout, pcfg.r
+    flops = 2 * M * K * Nout + 2 * m_g * K * r + 2 * m_g * r * Nout
+    g = torch.Generator(device=dev)
+    g.manual_seed(pcfg.seed + 7)
+    sets = []
+    for _ in range(PROJ_SETS):
+        x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        w = (torch.randn((Nout, K), generator=g, device=dev) * pcfg.w_sd).to(torch.bfloat16)
+        a = (torch.randn((r, K), generator=g, device=dev) * pcfg.w_sd).to(torch.bfloat16)
+        b = (torch.randn((Nout, r), generator=g, device=dev) * pcfg.w_sd).to(torch.bfloat16)
+        sets.append((x, w, isd.pack_proj_weights(w, a, b)))
+        del a, b
+    y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    gate = P["gate"]
+    warm = timed(lambda i: isd.gated_lora_proj_packed(P["x"], packed, gate, out=y))
+    cold = timed(lambda i: isd.gated_lora_proj_packed(sets[i % PROJ_SETS][0], sets[i % PROJ_SETS][2], gate, out=y))
+    lib_warm = timed(lambda i: torch.nn.functional.linear(P["x"], P["w"]))
+    lib_cold = timed(lambda i: torch.nn.functional.linear(sets[i % PROJ_SETS][0], sets[i % PROJ_SETS][1]))
+    del sets
+    torch.cuda.empty_cache()
+    frac = lambda us, f: round(f / (us * 1e-6) / 2.5e15, 4)
+    base_flops = 2 * M * K * Nout
+    return {"gated_warm_us": round(warm, 2), "gated_cold_us": round(cold, 2),
+            "mfma_frac_warm": frac(warm, flops), "mfma_frac_cold": frac(cold, flops),
+            "rotated_sets": PROJ_SETS, "alg_flops": flops,
+            "reference_hipblaslt_base_only_warm_us": round(lib_warm, 2),
+            "reference_hipblaslt_base_only_cold_us": round(lib_cold, 2),
+            "reference_hipblaslt_mfma_frac_cold": frac(lib_cold, base_flops)}
+
+
+def verify_parity_counts(vsets_host, vouts, N):
+    """The timed verification outputs of every input set against the oracle on the same
+    inputs: draws the oracle flags as within 1e-6 of a threshold (and what follows them
+    in the request) are excluded and counted; every other decision and id is compared.
+    Returns the counts; `mismatches` must be 0."""
     import oracle
+    compared = excluded = mism = 0
+    for v, out in zip(vsets_host, vouts):
+        ref = oracle.verify_step(v.logits, v.draft_logits, v.draft_ids, v.uniforms, N)
+        g = {k: t.cpu().numpy() for k, t in out.items()}
+        mism += int(np.count_nonzero(g["argmax_ids"] != ref["argmax_ids"]))
+        compared += g["argmax_ids"].size
+        for b in range(ref["n_accept"].shape[0]):
+            n_ref = int(ref["n_accept"][b])
+            evaluated = min(n_ref + 1, N - 1)
+            flagged = [i for i in range(evaluated) if ref["accept_flag"][b, i]]
+            upto = flagged[0] if flagged else evaluated
+            mism += int(np.count_nonzero(g["accept"][b, :upto] != ref["accept"][b, :upto]))
+            compared += upto
+            if flagged:
+                excluded += 1
+            else:
+                mism += int(g["n_accept"][b] != n_ref) + int(np.any(g["accept"][b] != ref["accept"][b]))
+                compared += 1
+                if ref["residual_flag"][b]:
+                    excluded += 1
+                else:
+                    mism += int(g["next_token"][b] != ref["next_token"][b])
+                    compared += 1
+            for j in range(N):
+                if ref["sample_flag"][b, j]:
+                    excluded += 1
+                else:
+                    mism += int(g["sampled_ids"][b, j] != ref["sampled_ids"][b, j])
+                    compared += 1
+    return {"sets": len(vsets_host), "compared": compared, "excluded_draws": excluded,
+            "excluded_frac": round(excluded / max(1, compared + excluded), 6), "mismatches": mism}
+
+
+# The all-core oracle baseline: worker processes forked before the GPU is touched, each
+# holding the host inputs (inherited at the fork) and one BLAS thread.
+_POOL_DATA = None
+
+
+def _pool_init():
+    from threadpoolctl import threadpool_limits
+    global _POOL_LIMIT
+    _POOL_LIMIT = threadpool_limits(1)
+
+
+def _w_proj(rows):
+    import oracle
+    att, ver, pin, scfg = _POOL_DATA
+    oracle.gated_lora_proj(pin.x[rows], pin.w, pin.a, pin.b, pin.gate[rows])
+    return len(rows)
+
+
+def _w_attention(b):
+    """One request: its own pages, under a page table that numbers them 0, 1, ..."""
+    import oracle
+    att, ver, pin, scfg = _POOL_DATA
+    s = slice(b, b + 1)
+    n = (int(att.ctx_lens[b]) + scfg.R + 15) // 16
+    pages = att.page_table[b, :n]
+    oracle.attention_step(att.q[s], att.k_new[s], att.v_new[s], att.k_pages[pages], att.v_pages[pages],
+                          np.arange(n, dtype=np.int32)[None], att.ctx_lens[s], att.scale)
+    return b
+
+
+def _w_verify(b):
+    import oracle
+    att, ver, pin, scfg = _POOL_DATA
+    s = slice(b, b + 1)
+    oracle.verify_step(ver.logits[s], ver.draft_logits[s], ver.draft_ids[s], ver.uniforms[s], scfg.N)
+    return b
+
+
+def _w_info(_):
+    from threadpoolctl import threadpool_info
+    return [{k: i.get(k) for k in ("internal_api", "version", "num_threads")} for i in threadpool_info()]
+
+
+def pool_workers() -> int:
+    """Worker count: the cores this process may run on, capped at 16 (a one-GPU share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_pool(att, ver, pin, scfg):
+    import multiprocessing as mp
+    global _POOL_DATA
+    _POOL_DATA = (att, ver, pin, scfg)
+    return mp.get_context("fork").Pool(pool_workers(), initializer=_pool_init)
+
+
+def cpu_baseline(scfg, att, ver, pin, pool, one_core_steps=1, all_core_steps=4):
+    """The oracle, as it is, on the host: whole steps of the benchmark workload (the
+    projection, attention and verification of all 64 requests, first verification input
+    set).  One core: in this process with one BLAS thread.  All cores: the same step
+    spread over a pool of worker processes, one BLAS thread each -- the projection by
+    row blocks, attention and verification by request.  `value` is the all-core rate."""
+    import oracle
+    from threadpoolctl import threadpool_limits
     t_proj = t_att = t_ver = 0.0
-    reps = 0
-    while reps == 0 or t_proj + t_att + t_ver < min_seconds:
-        t0 = time.perf_counter()
-        oracle.gated_lora_proj(pin.x, pin.w, pin.a, pin.b, pin.gate)
-        t1 = time.perf_counter()
-        oracle.attention_step(att.q, att.k_new, att.v_new, att.k_pages, att.v_pages,
-                              att.page_table, att.ctx_lens, att.scale)
-        t2 = time.perf_counter()
-        oracle.verify_step(ver.logits, ver.draft_logits, ver.draft_ids, ver.uniforms, scfg.N)
-        t3 = time.perf_counter()
-        t_proj, t_att, t_ver = t_proj + t1 - t0, t_att + t2 - t1, t_ver + t3 - t2
-        reps += 1
-    total = t_proj + t_att + t_ver
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(reps / total, 4), "unit": "steps/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"{reps} whole step(s) of the benchmark workload ({scfg.B} requests: "
-                       f"projection, attention, verification), {total:.1f} s"),
-            "seconds_per_step": {"proj": round(t_proj / reps, 3), "attention": round(t_att / reps, 3),
-                                 "verify": round(t_ver / reps, 3)}}
+    with threadpool_limits(1):
+        for _ in range(one_core_steps):
+            t0 = time.perf_counter()
+            oracle.gated_lora_proj(pin.x, pin.w, pin.a, pin.b, pin.gate)
+            t1 = time.perf_counter()
+            oracle.attention_step(att.q, att.k_new, att.v_new, att.k_pages, att.v_pages,
+                                  att.page_table, att.ctx_lens, att.scale)
+            t2 = time.perf_counter()
+            oracle.verify_step(ver.logits, ver.draft_logits, ver.draft_ids, ver.uniforms, scfg.N)
+            t3 = time.perf_counter()
+            t_proj, t_att, t_ver = t_proj + t1 - t0, t_att + t2 - t1, t_ver + t3 - t2
+    one = t_proj + t_att + t_ver
+    nw = pool._processes
+    blocks = [np.arange(i, min(i + 28, pin.x.shape[0])) for i in range(0, pin.x.shape[0], 28)]
+    pool.map(_w_info, range(nw))                      # workers up and initialised
+    t0 = time.perf_counter()
+    for _ in range(all_core_steps):
+        pool.map(_w_proj, blocks, chunksize=1)
+        pool.map(_w_attention, range(scfg.B), chunksize=1)
+        pool.map(_w_verify, range(scfg.B), chunksize=1)
+    allc = time.perf_counter() - t0
+    return {"value": round(all_core_steps / allc, 4), "unit": "steps/s", "cores": nw, "kind": "oracle",
+            "sample": (f"{all_core_steps} whole steps of the benchmark workload ({scfg.B} requests: projection, "
+                       f"attention, verification) over {nw} worker processes, {allc:.1f} s; one core: "
+                       f"{one_core_steps} step(s), {one:.1f} s"),
+            "one_core": {"value": round(one_core_steps / one, 4), "unit": "steps/s", "cores": 1,
+                         "seconds_per_step": {"proj": round(t_proj / one_core_steps, 3),
+                                              "attention": round(t_att / one_core_steps, 3),
+                                              "verify": round(t_ver / one_core_steps, 3)}},
+            "all_cores_seconds_per_step": round(allc / all_core_steps, 3)}
+
+
+def cpu_host_info(pool):
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "workers": pool._processes, "numpy": np.__version__, "blas": pool.map(_w_info, [0])[0]}
 
 
 if __name__ == "__main__":

@@ -3,6 +3,8 @@
   python -m strided_verify_propose_amd.profsum trace <kernel_stats.csv> <out.txt> "<command>"
   python -m strided_verify_propose_amd.profsum hbm <fetch counter_collection.csv>
       <write counter_collection.csv> <out.txt> "<fetch command>" "<write command>"
+  python -m strided_verify_propose_amd.profsum mfma <counter_collection.csv> <out.txt> "<command>"
+  python -m strided_verify_propose_amd.profsum sweep <sweep.jsonl> <out.txt> "<command>"
 
 The HBM summary scales each kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a 1 GiB device-to-device copy in the same run, and
@@ -106,6 +108,59 @@ def hbm(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+XCDS = 8           # GRBM_GUI_ACTIVE is summed over the XCDs; the busy time of one is the sum / 8
+SIMDS = 1024       # 256 CUs x 4 SIMDs
+CLOCK_GHZ = 2.4
+
+
+def mfma(counter_csv, out, command):
+    """MFMA activity per kernel: bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the
+    MFMA pipes' busy share (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x GPU-busy cycles of one
+    XCD), and the flop rate over that busy time against the 2.5 PFLOP/s bf16 peak."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["# MFMA counters per dispatch (rocprofv3 --pmc), mean over dispatches", f"command: {command}", "",
+             f"{'kernel':60s} {'n':>3s} {'GFLOP':>9s} {'gui_us':>8s} {'mfma_busy':>10s} {'PFLOP/s':>8s} {'frac':>6s}"]
+    for k, c in vals.items():
+        if "isd::" not in k:
+            continue
+        mean = {n: sum(v) / len(v) for n, v in c.items()}
+        flops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        gui = mean.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * gui) if gui else 0.0
+        us = gui / (CLOCK_GHZ * 1e3)
+        rate = flops / (us * 1e-6) / 1e15 if us else 0.0
+        n = len(next(iter(c.values())))
+        lines.append(f"{short(k)[:60]:60s} {n:3d} {flops / 1e9:9.3f} {us:8.2f} {100 * busy:9.1f}% {rate:8.3f} "
+                     f"{rate / 2.5:6.3f}")
+    lines += ["", "gui_us: GRBM_GUI_ACTIVE / 8 XCDs at 2.4 GHz (the dispatch under the profiler, serialised);",
+              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x gui cycles); frac: PFLOP/s / 2.5."]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def sweep(jsonl, out, command):
+    """The concurrency sweep's JSON lines as a table."""
+    import json
+    rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    lines = ["# Concurrency sweep: whole ISD step (projection, attention, verification) per C and N",
+             f"command: {command}", "",
+             f"{'p':>4s} {'N':>2s} {'C':>4s} {'ms/step':>8s} {'steps/s':>8s} {'tokens/s':>9s} {'p_hat':>6s} "
+             f"{'TPF':>6s} {'proj_us':>8s} {'attn_us':>8s} {'ver_us':>8s} {'attn%HBM':>8s} {'ver%HBM':>8s} "
+             f"{'proj%MFMA':>9s}"]
+    for r in rows:
+        u = r["us"]
+        lines.append(f"{r.get('acceptance_target', 0.9):4.1f} {r['stride_N']:2d} {r['C']:4d} {r['ms_per_step']:8.4f} "
+                     f"{r['steps_per_s']:8.1f} {r['tokens_per_s']:9.0f} {r['p_hat']:6.3f} "
+                     f"{r['tpf_closed_form_at_p_hat']:6.3f} {u['gated_lora_proj']:8.2f} {u['attention']:8.2f} "
+                     f"{u['verify']:8.2f} {100 * r['attention_hbm_frac']:8.1f} {100 * r['verify_hbm_frac']:8.1f} "
+                     f"{100 * r['proj_mfma_frac']:9.1f}")
+    if rows:
+        lines += ["", f"proposal noise sd: " + ", ".join(
+            sorted({f"{r.get('acceptance_target')}: {r.get('proposal_noise_sd')}" for r in rows}))]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def read_attention_traffic(path):
     """HBM bytes of one isd_attention_step (both kernels) from a summary, or None if the
     summary is absent or was taken on other attention sources."""
@@ -127,5 +182,9 @@ if __name__ == "__main__":
         trace(*sys.argv[2:5])
     elif sys.argv[1] == "hbm":
         hbm(*sys.argv[2:7])
+    elif sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:5])
+    elif sys.argv[1] == "sweep":
+        sweep(*sys.argv[2:5])
     else:
         raise SystemExit(__doc__)
