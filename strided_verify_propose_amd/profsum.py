@@ -108,34 +108,35 @@ def hbm(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
-XCDS = 8           # GRBM_GUI_ACTIVE is summed over the XCDs; the busy time of one is the sum / 8
 SIMDS = 1024       # 256 CUs x 4 SIMDs
 CLOCK_GHZ = 2.4
 
 
 def mfma(counter_csv, out, command):
-    """MFMA activity per kernel: bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the
-    MFMA pipes' busy share (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x GPU-busy cycles of one
-    XCD), and the flop rate over that busy time against the 2.5 PFLOP/s bf16 peak."""
+    """MFMA activity per kernel: bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) and
+    the MFMA pipes' busy cycles (SQ_VALU_MFMA_BUSY_CYCLES, summed over the 1024 SIMDs),
+    against the dispatch's own duration in the same run (its start and end timestamps):
+    busy share = busy cycles / (1024 x duration x 2.4 GHz), rate = flops / duration
+    against the 2.5 PFLOP/s bf16 peak."""
     vals = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(dict)
     for r in csv.DictReader(open(counter_csv)):
         vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[r["Kernel_Name"]][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
     lines = ["# MFMA counters per dispatch (rocprofv3 --pmc), mean over dispatches", f"command: {command}", "",
-             f"{'kernel':60s} {'n':>3s} {'GFLOP':>9s} {'gui_us':>8s} {'mfma_busy':>10s} {'PFLOP/s':>8s} {'frac':>6s}"]
+             f"{'kernel':60s} {'n':>3s} {'GFLOP':>9s} {'dur_us':>8s} {'mfma_busy':>10s} {'PFLOP/s':>8s} {'frac':>6s}"]
     for k, c in vals.items():
         if "isd::" not in k:
             continue
         mean = {n: sum(v) / len(v) for n, v in c.items()}
         flops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
-        gui = mean.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
-        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * gui) if gui else 0.0
-        us = gui / (CLOCK_GHZ * 1e3)
+        us = sum(dur[k].values()) / len(dur[k])
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * us * CLOCK_GHZ * 1e3) if us else 0.0
         rate = flops / (us * 1e-6) / 1e15 if us else 0.0
-        n = len(next(iter(c.values())))
-        lines.append(f"{short(k)[:60]:60s} {n:3d} {flops / 1e9:9.3f} {us:8.2f} {100 * busy:9.1f}% {rate:8.3f} "
-                     f"{rate / 2.5:6.3f}")
-    lines += ["", "gui_us: GRBM_GUI_ACTIVE / 8 XCDs at 2.4 GHz (the dispatch under the profiler, serialised);",
-              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x gui cycles); frac: PFLOP/s / 2.5."]
+        lines.append(f"{short(k)[:60]:60s} {len(dur[k]):3d} {flops / 1e9:9.3f} {us:8.2f} {100 * busy:9.1f}% "
+                     f"{rate:8.3f} {rate / 2.5:6.3f}")
+    lines += ["", "dur_us: the dispatch's end - start timestamps under the profiler (dispatches serialised);",
+              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x dur x 2.4 GHz); frac: PFLOP/s / 2.5."]
     open(out, "w").write("\n".join(lines) + "\n")
 
 
