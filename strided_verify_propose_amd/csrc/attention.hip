@@ -43,17 +43,21 @@ __device__ __forceinline__ int page_id(const int32_t* pt, int j, int num_pages) 
   return min(max(pt[j], 0), num_pages - 1);
 }
 
-// Query rows handled per wave, waves per group and wave groups per workgroup.  Each wave
-// keeps up to two 16-row query blocks in registers.  With at most two blocks one group of
-// eight waves deals the pages (one workgroup per CU, so no CU splits its time between two
-// workgroups); with more blocks (many query heads per KV head) two groups of four waves
-// each take half of them and read the same pages, the repeats hitting cache.
+// Query rows handled per wave, waves per group and wave groups per workgroup.  Every wave
+// keeps all the KV head's 16-row query blocks in registers, so every K/V byte is read from
+// memory once.  With at most two blocks one group of eight waves deals the pages (two
+// waves per SIMD; one workgroup per CU, so no CU splits its time between two workgroups);
+// with three or four blocks (many query heads per KV head) one group of four waves, one
+// per SIMD with the whole register file: two groups that split the blocks between them
+// and deal the same pages fetched every page twice from HBM (the pairs' loads go out
+// together and both miss).
 template <int D, int NQB>
 struct AttnShape {
-  static constexpr int QB = NQB < 2 ? NQB : 2;
-  static constexpr int GROUPS = (NQB + QB - 1) / QB;
-  static constexpr int WPG = (GROUPS == 1 && D / 16 >= 8) ? 8 : 4;  // waves per group
+  static constexpr int QB = NQB;
+  static constexpr int GROUPS = 1;
+  static constexpr int WPG = (NQB <= 2 && D / 16 >= 8) ? 8 : 4;  // waves per group
   static constexpr int THREADS = 64 * WPG * GROUPS;
+  static constexpr int MIN_BLOCKS = NQB <= 2 ? 2 : 1;           // workgroups per CU the registers allow
 };
 
 // One 16-token tile (a cached page or the block) against this wave's query blocks.
@@ -208,7 +212,7 @@ __device__ __forceinline__ int range_lo(int w, int T, int W) {
 }
 
 template <int D, int NQB>
-__global__ __launch_bounds__((AttnShape<D, NQB>::THREADS), 2)
+__global__ __launch_bounds__((AttnShape<D, NQB>::THREADS), (AttnShape<D, NQB>::MIN_BLOCKS))
 void attn_bf16_kernel(const AttnLaunch a) {
   constexpr int QB = AttnShape<D, NQB>::QB;
   constexpr int GROUPS = AttnShape<D, NQB>::GROUPS;
