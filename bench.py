@@ -105,7 +105,7 @@ def main():
     import torch
 
     from strided_verify_propose_amd import isd, synth
-    from strided_verify_propose_amd.profsum import read_attention_traffic
+    from strided_verify_propose_amd.profsum import read_attention_traffic, read_mfma
 
     dev = torch.device("cuda:0")
 
@@ -298,6 +298,10 @@ def main():
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
         "proj_alone": proj_alone,
+        # MFMA busy share and bf16 flops from rocprofv3 counters (profiles/), when they were
+        # taken on the current projection sources
+        "proj_mfma_counters": read_mfma(os.path.join(ROOT, "profiles", f"isd_step_{scfg.name}_mfma.txt"),
+                                        ("base_kernel_packed", "lora_kernel")),
         "roofline": {"bound": "hbm",
                      "kernel": "isd_attention_step (attn_bf16_kernel + attn_combine_kernel)",
                      "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -47,6 +47,21 @@ def attention_source_hash() -> str:
     return h.hexdigest()
 
 
+PROJ_SOURCES = ["csrc/gemm.hip", "csrc/gemm_packed.hip", "csrc/gemm_big.hip", "csrc/device.h", "csrc/tiles.h"]
+
+
+def source_hash(files) -> str:
+    """SHA-256 of source files with comments and blank lines removed."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            for line in fh.read().splitlines():
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def short(name: str) -> str:
     name = name.replace("isd::(anonymous namespace)::", "")
     if name.startswith("void "):
@@ -136,8 +151,28 @@ def mfma(counter_csv, out, command):
         lines.append(f"{short(k)[:60]:60s} {len(dur[k]):3d} {flops / 1e9:9.3f} {us:8.2f} {100 * busy:9.1f}% "
                      f"{rate:8.3f} {rate / 2.5:6.3f}")
     lines += ["", "dur_us: the dispatch's end - start timestamps under the profiler (dispatches serialised);",
-              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x dur x 2.4 GHz); frac: PFLOP/s / 2.5."]
+              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x dur x 2.4 GHz); frac: PFLOP/s / 2.5.",
+              f"projection_source_sha256: {source_hash(PROJ_SOURCES)}"]
     open(out, "w").write("\n".join(lines) + "\n")
+
+
+def read_mfma(path, kernel_prefixes):
+    """{kernel: {"gflop", "dur_us", "mfma_busy", "frac"}} for the kernels named, from an
+    MFMA summary taken on the current projection sources, else None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    kv = dict(l.split(":", 1) for l in text if l.startswith("projection_source_sha256:"))
+    if kv.get("projection_source_sha256", "").strip() != source_hash(PROJ_SOURCES):
+        return None
+    res = {}
+    for line in text:
+        for k in kernel_prefixes:
+            if line.startswith(k):
+                f = line[60:].split()
+                res[k] = {"gflop": float(f[1]), "dur_us": float(f[2]), "mfma_busy": float(f[3].rstrip("%")) / 100,
+                          "frac": float(f[5])}
+    return res or None
 
 
 def sweep(jsonl, out, command):

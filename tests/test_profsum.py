@@ -43,3 +43,24 @@ def test_hash_tracks_the_kernel_source(tmp_path, monkeypatch):
     att = tmp_path / "csrc" / "attention.hip"
     att.write_text(att.read_text() + "\nnamespace isd { int probe_symbol = 1; }\n")
     assert profsum.attention_source_hash() != h0
+
+
+def test_mfma_summary_is_read_only_for_the_current_projection_sources(tmp_path, monkeypatch):
+    for f in profsum.PROJ_SOURCES:
+        dst = tmp_path / f
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(profsum.ROOT, f), dst)
+    monkeypatch.setattr(profsum, "ROOT", str(tmp_path))
+    csv_path = tmp_path / "c.csv"
+    csv_path.write_text(
+        '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n'
+        '1,"isd::(anonymous namespace)::lora_kernel(isd::ProjLaunch)","SQ_INSTS_VALU_MFMA_MOPS_BF16",1000000,0,10000\n'
+        '1,"isd::(anonymous namespace)::lora_kernel(isd::ProjLaunch)","SQ_VALU_MFMA_BUSY_CYCLES",2457600,0,10000\n')
+    out = tmp_path / "m.txt"
+    profsum.mfma(str(csv_path), str(out), "cmd")
+    got = profsum.read_mfma(str(out), ("lora_kernel",))
+    assert got["lora_kernel"]["gflop"] == 0.512 and got["lora_kernel"]["dur_us"] == 10.0
+    assert abs(got["lora_kernel"]["mfma_busy"] - 0.1) < 1e-9        # 2457600 / (1024 x 10 us x 2.4 GHz)
+    g = tmp_path / "csrc" / "gemm.hip"
+    g.write_text(g.read_text() + "\nnamespace isd { int probe = 1; }\n")
+    assert profsum.read_mfma(str(out), ("lora_kernel",)) is None
