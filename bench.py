@@ -255,6 +255,7 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * 5 * (1 << 29) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    ceilings = attainable_bandwidth(dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -295,6 +296,7 @@ def main():
                                    for k, x in (("gated_lora_proj", proj_ms), ("attention", att_ms),
                                                 ("verify", ver_ms))},
         "device_copy_GBps": round(copy_gbps, 1),
+        "attainable_GBps": ceilings,
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
         "proj_alone": proj_alone,
@@ -712,6 +714,40 @@ def projection_alone(P, packed, pcfg, m_g, dev, reps=48):
             "reference_hipblaslt_base_only_warm_us": round(lib_warm, 2),
             "reference_hipblaslt_base_only_cold_us": round(lib_cold, 2),
             "reference_hipblaslt_mfma_frac_cold": frac(lib_cold, base_flops)}
+
+
+def attainable_bandwidth(dev):
+    """What the machine's HBM delivers to torch's own kernels, as context for the rooflines:
+    a streaming read (a sum over 1 GiB of bf16) and a gather of randomly placed 4 KB rows
+    (index_select over 512 MiB of rows, read + write counted) -- the access pattern of
+    paged K/V tiles.  HIP events around 5 calls each, after one warm-up."""
+    import torch
+
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    x = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
+    t_read = timed(lambda: x.sum(dtype=torch.float32))
+    del x
+    rows = torch.empty((1 << 17, 2048), dtype=torch.bfloat16, device=dev).normal_()   # 4 KB rows
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    perm = torch.randperm(rows.shape[0], generator=g, device=dev)
+    out = torch.empty_like(rows)
+    t_gather = timed(lambda: torch.index_select(rows, 0, perm, out=out))
+    nbytes = rows.numel() * 2
+    del rows, out, perm
+    torch.cuda.empty_cache()
+    return {"stream_read": round((1 << 30) / t_read / 1e9, 1),
+            "gather_4k_rows_read_write": round(2 * nbytes / t_gather / 1e9, 1)}
 
 
 def verify_parity_counts(vsets_host, vouts, N):
