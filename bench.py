@@ -717,10 +717,10 @@ def projection_alone(P, packed, pcfg, m_g, dev, reps=48):
 
 
 def attainable_bandwidth(dev):
-    """What the machine's HBM delivers to torch's own kernels, as context for the rooflines:
-    a streaming read (a sum over 1 GiB of bf16) and a gather of randomly placed 4 KB rows
-    (index_select over 512 MiB of rows, read + write counted) -- the access pattern of
-    paged K/V tiles.  HIP events around 5 calls each, after one warm-up."""
+    """What the machine's HBM delivers to torch's own kernels, as context for the rooflines: a
+    gather of randomly placed 4 KB rows (index_select over 512 MiB of rows, read + write
+    counted) -- the access pattern of paged K/V tiles -- next to the plain device copy.
+    HIP events around 5 calls, after one warm-up."""
     import torch
 
     def timed(fn, n=5):
@@ -734,9 +734,6 @@ def attainable_bandwidth(dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / n
 
-    x = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
-    t_read = timed(lambda: x.sum(dtype=torch.float32))
-    del x
     rows = torch.empty((1 << 17, 2048), dtype=torch.bfloat16, device=dev).normal_()   # 4 KB rows
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -746,8 +743,7 @@ def attainable_bandwidth(dev):
     nbytes = rows.numel() * 2
     del rows, out, perm
     torch.cuda.empty_cache()
-    return {"stream_read": round((1 << 30) / t_read / 1e9, 1),
-            "gather_4k_rows_read_write": round(2 * nbytes / t_gather / 1e9, 1)}
+    return {"gather_4k_rows_read_write": round(2 * nbytes / t_gather / 1e9, 1)}
 
 
 def verify_parity_counts(vsets_host, vouts, N):
