@@ -211,6 +211,19 @@ __device__ __forceinline__ int range_lo(int w, int T, int W) {
   return (int)(((long long)w * T) / W);
 }
 
+// Workgroup whose share of the cost list [range_lo(w), range_lo(w + 1)) holds position x.
+__device__ __forceinline__ int holder(int x, int T, int W) {
+  int w = (int)min<long long>(W - 1, ((long long)(x + 1) * W + T - 1) / T - 1);
+  while (w > 0 && range_lo(w, T, W) > x) --w;
+  while (w + 1 < W && range_lo(w + 1, T, W) <= x) ++w;
+  return w;
+}
+
+// Record of the split item whose first piece a workgroup holds (at most one: the item its
+// share ends inside), for the merge kernel: request, KV head, start of the item's cost
+// interval, end of its real units, total cost.
+constexpr int REC_INTS = ATTN_REC_INTS;
+
 template <int D, int NQB>
 __global__ __launch_bounds__((AttnShape<D, NQB>::THREADS), (AttnShape<D, NQB>::MIN_BLOCKS))
 void attn_bf16_kernel(const AttnLaunch a) {
@@ -244,6 +257,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
   const size_t rstride = (size_t)Hkv * D;  // between consecutive block rows
 
   int first = 1;  // no piece processed yet (selects the partial-result slot)
+  if (threadIdx.x == 0) a.rec[w * REC_INTS] = -1;  // no split item starts here (unless found below)
   for (int cur = lo; cur < hi;) {
     // the item (b, kvh) holding cost position `cur`, and this workgroup's piece of it
     const int b = find_request(pre, a.B, cur);
@@ -255,6 +269,14 @@ void attn_bf16_kernel(const AttnLaunch a) {
     const int unit0 = max(cur - istart, 0), unit1 = seg_end - istart;
     cur = seg_end;
     if (unit1 <= unit0) continue;  // the range covers only this item's start-up share
+    if (unit0 == 0 && unit1 < u && threadIdx.x == 0) {  // the first piece of a split item
+      int* r = a.rec + w * REC_INTS;
+      r[0] = b;
+      r[1] = kvh;
+      r[2] = istart - ITEM_COST;
+      r[3] = istart + u;
+      r[4] = T;
+    }
     const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
     const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
     const size_t hoff = (size_t)kvh * tile;
@@ -306,7 +328,10 @@ void attn_bf16_kernel(const AttnLaunch a) {
     u32x4 kf[D / 32], kf2[D / 32];
     u32x2 vf[D / 16], vf2[D / 16];
 
+    int blk_page0 = 0, blk_page1 = 0;  // pages of the block's first and last slot
     if (do_block) {  // the block's own rows, from k_new / v_new (rows past R zeroed)
+      blk_page0 = page_id(pt, L / PAGE, a.num_pages);
+      blk_page1 = page_id(pt, (L + R - 1) / PAGE, a.num_pages);
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
         kf2[c] = *reinterpret_cast<const u32x4*>(kn_ + blk + min(l16, R - 1) * rstride + 32 * c + 8 * g);
@@ -336,7 +361,31 @@ void attn_bf16_kernel(const AttnLaunch a) {
       load_kv_page<D>(kc + t, vc + t, lane, kf, vf);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (do_block) attend_tile<D, QB, 2>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, 0, G, lane);
+    if (do_block) {
+      // The append: the block's rows, already in this wave's registers, go to their page
+      // slots ctx_len + r.  No piece reads those slots from the cache (the block is read
+      // from k_new / v_new, and slots past the context are masked in the partial page), so
+      // the stores may land at any time during the kernel.
+      uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
+      uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
+      if (l16 < R) {
+        const int j = L + l16;
+        const size_t base = page_off(j / PAGE == L / PAGE ? blk_page0 : blk_page1);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          *reinterpret_cast<u32x4*>(kcw + base + (4 * c + g) * 128 + (j % PAGE) * 8) = kf2[c];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (4 * g + t >= R) continue;
+        const int j = L + 4 * g + t, slot = j % PAGE;
+        const size_t base = page_off(j / PAGE == L / PAGE ? blk_page0 : blk_page1) + (slot / 4) * 64 + (slot % 4);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+          vcw[base + n * 256 + l16 * 4] = (uint16_t)(vf2[n][t >> 1] >> (16 * (t & 1)));
+      }
+      attend_tile<D, QB, 2>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, 0, G, lane);
+    }
     if (do_partial)
       attend_tile<D, QB, 1>(kf2, vf2, qf, qb0, NQB, o, m, l, scale_log2, L - nfull * PAGE, G, lane);
 
@@ -421,7 +470,9 @@ void attn_bf16_kernel(const AttnLaunch a) {
           u32x2 wv;
           wv[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
           wv[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
-          *reinterpret_cast<u32x2*>(out + (((size_t)b * R + r) * Hq + kvh * G + hg) * D + 16 * n + 4 * g) = wv;
+          // output row (b, r, head): below B R Hq <= 2048 * 15 * 65535 < 2^32
+          const unsigned orow = (unsigned)(b * R + r) * (unsigned)Hq + (unsigned)(kvh * G + hg);
+          *reinterpret_cast<u32x2*>(out + (size_t)orow * D + 16 * n + 4 * g) = wv;
         } else {
           *reinterpret_cast<f32x4*>(po + (size_t)qr * D + 16 * n + 4 * g) = acc;
         }
@@ -436,79 +487,26 @@ void attn_bf16_kernel(const AttnLaunch a) {
   }
 }
 
-// After every read of the cache: write the block's K/V rows into their page slots and
-// merge the pieces of items that crossed workgroup boundaries.  Which workgroups hold
-// pieces of an item, and in which of their two slots, follows from the same cost list
-// the main kernel split (rebuilt here from the context lengths): workgroup w holds a
-// piece iff its share meets the item's real units, in slot 2w + 1 if its share began
-// before the item (it already wrote a piece of an earlier item), else in slot 2w.  The
-// pieces are merged in workgroup order.
+// Merge the pieces of items that crossed workgroup boundaries.  Workgroup w of this grid
+// reads the record the main kernel's workgroup w wrote: the split item whose first piece
+// it held, if any.  The workgroups holding pieces of that item are w .. w1 (those whose
+// share meets the item's real units); each wrote its piece in slot 2k + 1 if its share
+// began before the item (it already wrote a piece of an earlier item), else in slot 2k.
+// The pieces are merged in workgroup order.
 constexpr int COMBINE_THREADS = 256;
 static_assert(COMBINE_THREADS == 4 * 64, "the combine's few-piece path maps thread -> (piece, row) as 4 x 64");
-constexpr int APPEND_V = 8;  // V elements of the block per thread (R * D <= 15 * 128 < 8 * 256)
 
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const AttnLaunch a, int W) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
+  const int w0 = blockIdx.x;
   const int tid = threadIdx.x;
-  // the block's K (16-byte units of 8 dims) and V (elements) go out with the context
-  // lengths; the page ids of their slots follow once the length is known
-  const int L = clamp_len(a, b);
-  const size_t rstride = (size_t)Hkv * D;
-  const size_t blk = ((size_t)b * R * Hkv + kvh) * D;
-  const uint16_t* kn_ = static_cast<const uint16_t*>(a.k_new);
-  const uint16_t* vn_ = static_cast<const uint16_t*>(a.v_new);
-  const int nk = R * (D / 8), nv = R * D;
-  u32x4 kval = u32x4{0u, 0u, 0u, 0u};
-  uint16_t vval[APPEND_V];
-  {
-    const int e = min(tid, nk - 1), t = e / (D / 8), d8 = e - t * (D / 8);
-    kval = *reinterpret_cast<const u32x4*>(kn_ + blk + t * rstride + d8 * 8);
-#pragma unroll
-    for (int q = 0; q < APPEND_V; ++q) {
-      const int ev = min(tid + q * COMBINE_THREADS, nv - 1), tv = ev / D, d = ev - tv * D;
-      vval[q] = vn_[blk + tv * rstride + d];
-    }
-  }
-  __shared__ int pre[MAX_B + 1];
-  build_prefix(a, pre);
-  const int T = pre[a.B];
-
-  // append (after every read of the cache: the main kernel has finished)
-  {
-    const int32_t* __restrict__ pt = a.page_table + (size_t)b * a.max_pages;
-    const size_t tile = (size_t)PAGE * D;
-    uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
-    uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    if (tid < nk) {
-      const int t = tid / (D / 8), d8 = tid - t * (D / 8), j = L + t;
-      const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-      *reinterpret_cast<u32x4*>(kcw + base + d8 * 128 + (j % PAGE) * 8) = kval;
-    }
-#pragma unroll
-    for (int q = 0; q < APPEND_V; ++q) {
-      const int ev = tid + q * COMBINE_THREADS;
-      if (ev >= nv) break;
-      const int tv = ev / D, d = ev - tv * D, j = L + tv, slot = j % PAGE;
-      const size_t base = ((size_t)page_id(pt, j / PAGE, a.num_pages) * Hkv + kvh) * tile;
-      vcw[base + (d / 16) * 256 + (slot / 4) * 64 + (d % 16) * 4 + slot % 4] = vval[q];
-    }
-  }
-
-  // this item's cost interval [c0, iend): start-up share, then its u real units
-  const int u = units_of(L);
-  const int c0 = pre[b] + kvh * (u + ITEM_COST), istart = c0 + ITEM_COST, iend = istart + u;
-  // workgroups whose shares meet [istart, iend): from the one holding istart to the one
-  // holding iend - 1 (largest w with range_lo(w) <= x)
-  auto holder = [&](int x) -> int {
-    int w = (int)min<long long>(W - 1, ((long long)(x + 1) * W + T - 1) / T - 1);
-    while (w > 0 && range_lo(w, T, W) > x) --w;
-    while (w + 1 < W && range_lo(w + 1, T, W) <= x) ++w;
-    return w;
-  };
-  const int w0 = holder(istart), w1 = holder(iend - 1);
-  if (w0 == w1) return;  // one workgroup held the whole item and wrote its output
+  const int* rec = a.rec + (size_t)w0 * REC_INTS;
+  const int b = rec[0];
+  if (b < 0) return;  // no split item starts in this workgroup's share
+  const int kvh = rec[1], c0 = rec[2], iend = rec[3], T = rec[4];
+  const int w1 = holder(iend - 1, T, W);  // the last workgroup holding a piece
+  const int istart = c0 + ITEM_COST;
+  const int R = a.R, G = a.G, Hq = a.Hq, RG = R * G;
   __shared__ int s_slots[2 * ATTN_MAX_WG];
   __shared__ int s_np;
   if (tid < 64) {
@@ -785,7 +783,7 @@ hipError_t launch_shape(const AttnLaunch& a, hipStream_t s) {
   W = std::min<long long>(W, std::max<long long>(1, (units_max + 15) / 16));
   W = std::min<long long>(W, ATTN_MAX_WG);
   attn_bf16_kernel<D, NQB><<<(int)W, NT, 0, s>>>(a);
-  attn_combine_kernel<D><<<dim3(a.Hkv, a.B), COMBINE_THREADS, 0, s>>>(a, (int)W);
+  attn_combine_kernel<D><<<(int)W, COMBINE_THREADS, 0, s>>>(a, (int)W);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- attention workspace
 struct AttnWs {
-  size_t part_o, part_ml, total;
+  size_t part_o, part_ml, rec, total;
 };
 
 AttnWs attn_ws(int N, int Hq, int Hkv, int D) {
@@ -30,7 +30,8 @@ AttnWs attn_ws(int N, int Hq, int Hkv, int D) {
   const size_t slots = (size_t)ATTN_MAX_WG * 2;
   w.part_o = 0;
   w.part_ml = align256(slots * RG * D * sizeof(float));
-  w.total = w.part_ml + align256(slots * RG * 2 * sizeof(float));
+  w.rec = w.part_ml + align256(slots * RG * 2 * sizeof(float));
+  w.total = w.rec + align256((size_t)ATTN_MAX_WG * ATTN_REC_INTS * sizeof(int32_t));
   return w;
 }
 
@@ -259,6 +260,7 @@ isd_status prepare_attention(isd_dtype dt, const void* q, const void* k_new, con
   char* ws = static_cast<char*>(workspace);
   a->part_o = ws ? reinterpret_cast<float*>(ws + w.part_o) : nullptr;
   a->part_ml = ws ? reinterpret_cast<float*>(ws + w.part_ml) : nullptr;
+  a->rec = ws ? reinterpret_cast<int32_t*>(ws + w.rec) : nullptr;
   return clear_error();
 }
 

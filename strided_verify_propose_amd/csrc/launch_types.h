@@ -25,10 +25,12 @@ struct AttnLaunch {
   // workspace carve-up: two partial slots per workgroup of the balanced grid
   float* part_o;         // [ATTN_MAX_WG * 2][R*G][D]
   float* part_ml;        // [ATTN_MAX_WG * 2][R*G][2]
+  int32_t* rec;          // [ATTN_MAX_WG][ATTN_REC_INTS] the split item whose first piece a workgroup holds
 };
 constexpr int ATTN_MAX_WG = 2048;  // workgroups of the balanced attention grid, at most
 constexpr int ATTN_MAX_B = 2048;   // requests per bf16 attention call
 constexpr int ATTN_PAGE = 16;      // tokens per page
+constexpr int ATTN_REC_INTS = 8;   // ints per workgroup record of a split item
 // Start-up cost of a piece of the balanced work list, in 16-token tiles: request b with
 // L_b cached tokens costs Hkv (ceil(L_b/16) + 1 + ATTN_ITEM_COST) units, and the sum over
 // the requests of a call is kept in 32-bit integers.
