@@ -19,8 +19,11 @@
 //     every workgroup of a grid sized to the resident capacity takes an equal contiguous
 //     share.  A workgroup writes the output of every item it holds whole, and an
 //     unnormalised partial (max, sum, O) for the at most two items cut by its share's
-//     edges; a second kernel merges those in workgroup order and appends the block's K/V
-//     to the cache after all reads.  No workgroup waits on or signals another.
+//     edges; a second kernel merges those in workgroup order.  No workgroup waits on or
+//     signals another.
+//   * The block's own K/V rows are read from k_new / v_new, and the wave that attends
+//     them also stores them into their cache slots.  No piece reads those slots as
+//     context, so the stores may land at any time.
 //   * Inside a workgroup the group's waves take the tiles of a piece round-robin (the
 //     block's own rows and the partial page first), keep the next page's loads in flight
 //     while using the current one, and merge their states through LDS in a fixed order,
