@@ -229,6 +229,9 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
  * isd_proj_packed_bytes: size of the packed buffer (0 for unsupported shapes).
  * isd_pack_proj_weights: writes the packed buffer from w [Nout,K], a [r,K], b [Nout,r]
  *   (a, b unused when r == 0); asynchronous on `stream`.
+ * isd_pack_proj_weights_kn: the same packed buffer, bit for bit, from the y = x W
+ *   storage w [K,Nout], a [K,r], b [r,Nout]; a caller holding weights in that
+ *   orientation packs them once without a transpose of its own.
  * isd_gated_lora_proj_packed: as isd_gated_lora_proj with the packed buffer in place of
  *   w, a, b; r is the rank the buffer was packed with (gate NULL => base only, any r).
  * Requires: K % 64 == 0 and 64 <= K <= 2^20, Nout % 128 == 0 and 128 <= Nout <= 2^20,
@@ -237,6 +240,8 @@ isd_status isd_gated_lora_proj(const void* x, const void* w, const void* a, cons
 size_t isd_proj_packed_bytes(int K, int Nout, int r);
 isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, void* packed, int K,
                                  int Nout, int r, void* stream);
+isd_status isd_pack_proj_weights_kn(const void* w, const void* a, const void* b, void* packed, int K,
+                                    int Nout, int r, void* stream);
 isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const uint8_t* gate,
                                       void* y, int M, int K, int Nout, int r, void* workspace,
                                       size_t workspace_bytes, void* stream);

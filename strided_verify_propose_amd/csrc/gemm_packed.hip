@@ -30,7 +30,12 @@ constexpr int FRAG = 64 * 8;                    // elements in one packed 16 x 3
 
 // ---------------------------------------------------------------- packing
 // One thread per 16 bytes of the packed buffer: S = [W^T; A^T] in fragment order, then
-// B^T as it is (the second kernel reads it row-major).
+// B^T as it is (the second kernel reads it row-major).  KN = false reads the
+// linear-layer storage w [Nout, K], a [r, K], b [Nout, r]; KN = true reads the
+// y = x W storage w [K, Nout], a [K, r], b [r, Nout] (eight strided 2-byte reads per
+// thread; sixteen lanes read sixteen consecutive columns of one row, and packing is done
+// once per weight set).
+template <bool KN>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w,
                                                    const uint16_t* __restrict__ a,
                                                    const uint16_t* __restrict__ b,
@@ -39,18 +44,34 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long gS = (long long)(Nout + r) * K / 8, gB = (long long)Nout * r / 8;
   if (g >= gS + gB) return;
+  u32x4 v;
   if (g >= gS) {
-    const long long h = g - gS;
-    *reinterpret_cast<u32x4*>(packed + (size_t)(Nout + r) * K + (size_t)h * 8) =
-        *reinterpret_cast<const u32x4*>(b + (size_t)h * 8);
+    const long long h = g - gS;  // elements 8h .. 8h + 7 of B^T: row n, ranks j .. j + 7
+    if constexpr (KN) {
+      const int n = (int)(h * 8 / r), j = (int)(h * 8 % r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (uint32_t)b[(size_t)(j + 2 * e) * Nout + n] | ((uint32_t)b[(size_t)(j + 2 * e + 1) * Nout + n] << 16);
+    } else {
+      v = *reinterpret_cast<const u32x4*>(b + (size_t)h * 8);
+    }
+    *reinterpret_cast<u32x4*>(packed + (size_t)(Nout + r) * K + (size_t)h * 8) = v;
     return;
   }
   const int lane = (int)(g & 63);
   const long long frag = g >> 6;
   const int kb = (int)(frag % (K / 32)), nb = (int)(frag / (K / 32));
-  const int row = nb * 16 + (lane & 15), col = kb * 32 + 8 * (lane >> 4);
-  const uint16_t* src = row < Nout ? w + (size_t)row * K + col : a + (size_t)(row - Nout) * K + col;
-  *reinterpret_cast<u32x4*>(packed + (size_t)g * 8) = *reinterpret_cast<const u32x4*>(src);
+  const int row = nb * 16 + (lane & 15), col = kb * 32 + 8 * (lane >> 4);  // S[row][col .. col + 7]
+  if constexpr (KN) {
+    const uint16_t* src = row < Nout ? w + (size_t)col * Nout + row : a + (size_t)col * r + (row - Nout);
+    const size_t ld = row < Nout ? (size_t)Nout : (size_t)r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (uint32_t)src[(2 * e) * ld] | ((uint32_t)src[(2 * e + 1) * ld] << 16);
+  } else {
+    const uint16_t* src = row < Nout ? w + (size_t)row * K + col : a + (size_t)(row - Nout) * K + col;
+    v = *reinterpret_cast<const u32x4*>(src);
+  }
+  *reinterpret_cast<u32x4*>(packed + (size_t)g * 8) = v;
 }
 
 // ---------------------------------------------------------------- product
@@ -250,9 +271,13 @@ hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_pack_proj(const uint16_t* w, const uint16_t* a, const uint16_t* b, uint16_t* packed,
-                            int K, int Nout, int r, hipStream_t s) {
+                            int K, int Nout, int r, bool kn, hipStream_t s) {
   const long long groups = (long long)(Nout + r) * K / 8 + (long long)Nout * r / 8;
-  pack_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(w, a, b, packed, K, Nout, r);
+  const unsigned grid = (unsigned)((groups + 255) / 256);
+  if (kn)
+    pack_kernel<true><<<grid, 256, 0, s>>>(w, a, b, packed, K, Nout, r);
+  else
+    pack_kernel<false><<<grid, 256, 0, s>>>(w, a, b, packed, K, Nout, r);
   return hipGetLastError();
 }
 

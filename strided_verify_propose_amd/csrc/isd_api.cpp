@@ -120,8 +120,18 @@ isd_status isd_pack_proj_weights(const void* w, const void* a, const void* b, vo
   if (st != ISD_OK) return st;
   return hip_status(isd::launch_pack_proj(static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(a),
                                           static_cast<const uint16_t*>(b), static_cast<uint16_t*>(packed), K,
-                                          Nout, r, as_stream(stream)),
+                                          Nout, r, false, as_stream(stream)),
                     "pack_proj_weights launch");
+}
+
+isd_status isd_pack_proj_weights_kn(const void* w, const void* a, const void* b, void* packed, int K,
+                                    int Nout, int r, void* stream) {
+  const isd_status st = isd::prepare_pack_proj(w, a, b, packed, K, Nout, r);
+  if (st != ISD_OK) return st;
+  return hip_status(isd::launch_pack_proj(static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(a),
+                                          static_cast<const uint16_t*>(b), static_cast<uint16_t*>(packed), K,
+                                          Nout, r, true, as_stream(stream)),
+                    "pack_proj_weights_kn launch");
 }
 
 isd_status isd_gated_lora_proj_packed(const void* x, const void* packed, const uint8_t* gate, void* y, int M,

@@ -24,7 +24,8 @@ hipError_t launch_lora(const ProjLaunch& p, hipStream_t s);  // the second kerne
 hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s);  // sum of the K parts
 hipError_t launch_proj_packed(const ProjLaunch& p, hipStream_t s);
 // Pack [W^T; A^T] (Nout + r rows of K) into fragment order and copy B^T after it.
+// kn: w [K, Nout], a [K, r], b [r, Nout] instead of w [Nout, K], a [r, K], b [Nout, r]
 hipError_t launch_pack_proj(const uint16_t* w, const uint16_t* a, const uint16_t* b, uint16_t* packed,
-                            int K, int Nout, int r, hipStream_t s);
+                            int K, int Nout, int r, bool kn, hipStream_t s);
 
 }  // namespace isd

@@ -26,7 +26,8 @@ EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_pack_kv_pages", "isd_unpack_kv_pages",
            "isd_verify_workspace_bytes", "isd_verify", "isd_verify_noalloc",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
-           "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_gated_lora_proj_packed",
+           "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_pack_proj_weights_kn",
+           "isd_gated_lora_proj_packed",
            "isd_commit", "isd_lm_head", "isd_lm_head_verify_workspace_bytes",
            "isd_lm_head_verify")
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.isd_proj_packed_bytes.argtypes = [i32] * 3
     L.isd_pack_proj_weights.restype = i32
     L.isd_pack_proj_weights.argtypes = [vp] * 4 + [i32] * 3 + [vp]
+    L.isd_pack_proj_weights_kn.restype = i32
+    L.isd_pack_proj_weights_kn.argtypes = [vp] * 4 + [i32] * 3 + [vp]
     L.isd_gated_lora_proj_packed.restype = i32
     L.isd_gated_lora_proj_packed.argtypes = [vp] * 4 + [i32] * 4 + [vp, sz, vp]
     L.isd_commit.restype = ctypes.c_int
@@ -354,6 +357,27 @@ def pack_proj_weights(w, a=None, b=None) -> PackedProj:
         raise IsdError(2, f"unsupported projection shape K={K} Nout={Nout} r={r}")
     data = torch.empty(nbytes // 2, dtype=bf, device=dev)
     _check(L.isd_pack_proj_weights(_ptr(w), _ptr(a), _ptr(b), _ptr(data), K, Nout, r, _stream(dev)))
+    return PackedProj(data, K, Nout, r)
+
+
+def pack_proj_weights_kn(w, a=None, b=None) -> PackedProj:
+    """The same packed weights from the y = x W storage: w [K,Nout], a [K,r], b [r,Nout]
+    (isd_pack_proj_weights_kn; a, b None: base weights only)."""
+    K, Nout = w.shape
+    dev = w.device
+    bf = torch.bfloat16
+    _need(w, "w", bf, (K, Nout), dev)
+    r = 0
+    if a is not None or b is not None:
+        r = a.shape[1]
+        _need(a, "a", bf, (K, r), dev)
+        _need(b, "b", bf, (r, Nout), dev)
+    L = lib()
+    nbytes = L.isd_proj_packed_bytes(K, Nout, r)
+    if nbytes == 0:
+        raise IsdError(2, f"unsupported projection shape K={K} Nout={Nout} r={r}")
+    data = torch.empty(nbytes // 2, dtype=bf, device=dev)
+    _check(L.isd_pack_proj_weights_kn(_ptr(w), _ptr(a), _ptr(b), _ptr(data), K, Nout, r, _stream(dev)))
     return PackedProj(data, K, Nout, r)
 
 

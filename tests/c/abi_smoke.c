@@ -36,6 +36,8 @@ int main(void) {
         ISD_ERR_UNSUPPORTED);
   CHECK(isd_unpack_kv_pages(ISD_BF16, NULL, fake, (void*)0x3000, (void*)0x4000, 10, 8, 128, NULL) ==
         ISD_ERR_INVALID_ARG);
+  CHECK(isd_pack_proj_weights_kn(NULL, fake, fake, fake, 4096, 4096, 128, NULL) == ISD_ERR_INVALID_ARG);
+  CHECK(isd_pack_proj_weights_kn(fake, fake, fake, fake, 4096, 4100, 128, NULL) == ISD_ERR_UNSUPPORTED);
   if (fails == 0) printf("c abi ok\n");
   return fails == 0 ? 0 : 1;
 }

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -161,6 +161,7 @@ def test_proj_packed_bytes(L, K, Nout, r, ok):
 ])
 def test_pack_validation(L, args, status):
     assert L.isd_pack_proj_weights(*args, None) == status
+    assert L.isd_pack_proj_weights_kn(*args, None) == status
 
 
 def test_workspace_queries_grow_with_shape(L):

@@ -24,7 +24,12 @@ def run(M, K, Nout, r, seed, pattern=(0, 0, 0, 1, 1, 1, 1)):
     yp = isd.gated_lora_proj_packed(x, pk, gate)
     ybp = isd.gated_lora_proj_packed(x, pk)
     ybp0 = isd.gated_lora_proj_packed(x, isd.pack_proj_weights(w))
+    # packing from the y = x W storage gives the same buffer, byte for byte
+    pk_kn = isd.pack_proj_weights_kn(w.t().contiguous(), a.t().contiguous(), b.t().contiguous())
+    pk0, pk0_kn = isd.pack_proj_weights(w), isd.pack_proj_weights_kn(w.t().contiguous())
     torch.cuda.synchronize()
+    assert torch.equal(pk_kn.data.view(torch.int16), pk.data.view(torch.int16)), "packed from [K, Nout] differs"
+    assert torch.equal(pk0_kn.data.view(torch.int16), pk0.data.view(torch.int16)), "base-only packing differs"
     assert torch.equal(y, y2), "not deterministic"
     assert torch.equal(yp, y), "packed path differs from the row-major path"
     assert torch.equal(ybp, yb) and torch.equal(ybp0, yb), "packed base-only path differs"
