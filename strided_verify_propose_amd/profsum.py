@@ -5,6 +5,8 @@
       <write counter_collection.csv> <out.txt> "<fetch command>" "<write command>"
   python -m strided_verify_propose_amd.profsum mfma <counter_collection.csv> <out.txt> "<command>"
   python -m strided_verify_propose_amd.profsum sweep <sweep.jsonl> <out.txt> "<command>"
+  python -m strided_verify_propose_amd.profsum stalls <out.txt> <counter_collection.csv> "<command>"
+      [<counter_collection.csv> "<command>" ...]
 
 The HBM summary scales each kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
 what the same counters read for a 1 GiB device-to-device copy in the same run, and
@@ -197,6 +199,59 @@ def sweep(jsonl, out, command):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+STALL_SHARES = [  # (label, counter, denominator): wave-cycle shares and per-unit busy shares
+    ("waiting (any)", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+    ("waiting to issue", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("issuing", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("waiting to issue LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+]
+
+
+def stalls(out, *pairs):
+    """Per-kernel means of every counter in one or more rocprofv3 --pmc passes (one CSV
+    and its command per pass), as a table with one column per kernel, headed by the
+    wave-cycle shares above, the MFMA pipes' busy share (as in the MFMA summary) and the
+    share of time the CUs' L1 caches wait on data pending from L2
+    (TCP_PENDING_STALL_CYCLES over 256 CUs)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(dict)
+    cmds = []
+    for path, cmd in zip(pairs[0::2], pairs[1::2]):
+        cmds.append(cmd)
+        for r in csv.DictReader(open(path)):
+            if "isd::" not in r["Kernel_Name"]:
+                continue
+            vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[r["Kernel_Name"]][(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    kernels = sorted(vals, key=lambda n: -sum(dur[n].values()) / len(dur[n]))
+    mean = {k: {n: sum(v) / len(v) for n, v in vals[k].items()} for k in kernels}
+    us = {k: sum(dur[k].values()) / len(dur[k]) for k in kernels}
+    names = [short(k).split("(")[0].split("<")[0][:16] for k in kernels]
+    lines = ["# Wait and activity counters per dispatch (rocprofv3 --pmc), mean over dispatches"]
+    lines += [f"pass {i + 1} command: {c}" for i, c in enumerate(cmds)]
+    lines += ["", "kernels: " + "; ".join(f"{n} = {short(k)}" for n, k in zip(names, kernels)), "",
+              f"{'':34s}" + "".join(f"{n:>17s}" for n in names),
+              f"{'duration under the profiler, us':34s}" + "".join(f"{us[k]:17.2f}" for k in kernels)]
+
+    def row(label, f):
+        cells = []
+        for k in kernels:
+            v = f(mean[k], us[k])
+            cells.append(f"{v:17.1f}" if v is not None else f"{'-':>17s}")
+        lines.append(f"{label:34s}" + "".join(cells))
+
+    for label, num, den in STALL_SHARES:
+        row(f"% wave cycles {label}", lambda m, t, a=num, b=den: 100 * m[a] / m[b] if a in m and m.get(b) else None)
+    row("% MFMA pipes busy", lambda m, t: 100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * t * CLOCK_GHZ * 1e3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and t else None)
+    row("% L1 stalled on pending L2 data", lambda m, t: 100 * m["TCP_PENDING_STALL_CYCLES"] / (256 * t * CLOCK_GHZ * 1e3)
+        if "TCP_PENDING_STALL_CYCLES" in m and t else None)
+    lines.append("")
+    for n in sorted({c for k in kernels for c in mean[k]}):
+        lines.append(f"{n:34s}" + "".join(f"{mean[k][n]:17.6g}" if n in mean[k] else f"{'-':>17s}" for k in kernels))
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def read_attention_traffic(path):
     """HBM bytes of one isd_attention_step (both kernels) from a summary, or None if the
     summary is absent or was taken on other attention sources."""
@@ -222,5 +277,7 @@ if __name__ == "__main__":
         mfma(*sys.argv[2:5])
     elif sys.argv[1] == "sweep":
         sweep(*sys.argv[2:5])
+    elif sys.argv[1] == "stalls":
+        stalls(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)

@@ -64,3 +64,23 @@ def test_mfma_summary_is_read_only_for_the_current_projection_sources(tmp_path, 
     g = tmp_path / "csrc" / "gemm.hip"
     g.write_text(g.read_text() + "\nnamespace isd { int probe = 1; }\n")
     assert profsum.read_mfma(str(out), ("lora_kernel",)) is None
+
+
+def test_stall_summary_shares(tmp_path):
+    """Wave-cycle shares are the counters' ratios; passes are merged per kernel; busy and
+    stall shares are over the dispatch's own duration (10 us here)."""
+    k = '"isd::(anonymous namespace)::lora_kernel(isd::ProjLaunch)"'
+    head = '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n'
+    p1, p2 = tmp_path / "p1.csv", tmp_path / "p2.csv"
+    p1.write_text(head + f"1,{k},SQ_WAVE_CYCLES,1000,0,10000\n1,{k},SQ_WAIT_ANY,250,0,10000\n"
+                  f"1,{k},SQ_WAIT_INST_ANY,500,0,10000\n1,{k},SQ_ACTIVE_INST_ANY,250,0,10000\n")
+    p2.write_text(head + f"1,{k},SQ_VALU_MFMA_BUSY_CYCLES,4915200,0,10000\n"
+                  f"1,{k},TCP_PENDING_STALL_CYCLES,3072000,0,10000\n")
+    out = tmp_path / "s.txt"
+    profsum.stalls(str(out), str(p1), "cmd1", str(p2), "cmd2")
+    rows = {l[:34].strip(): l[34:].split() for l in out.read_text().splitlines() if len(l) > 34}
+    assert rows["% wave cycles waiting (any)"] == ["25.0"]
+    assert rows["% wave cycles waiting to issue"] == ["50.0"]
+    assert rows["% MFMA pipes busy"] == ["20.0"]                 # 4915200 / (1024 x 10 us x 2.4 GHz)
+    assert rows["% L1 stalled on pending L2 data"] == ["50.0"]   # 3072000 / (256 x 10 us x 2.4 GHz)
+    assert "pass 2 command: cmd2" in out.read_text()
