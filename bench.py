@@ -242,6 +242,7 @@ def main():
     # cache) and rotated over PROJ_SETS sets of activations and packed weights (cold), with
     # hipBLASLt's time for the base product (torch.nn.functional.linear) as a reference
     proj_alone = projection_alone(P, packed, pcfg, m_g, dev)
+    carried_q = verify_carried(vsets, vouts, N, dev)
 
     # measured device copy ceiling: a 512 MiB device-to-device copy, timed with events
     src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
@@ -300,6 +301,7 @@ def main():
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
         "proj_alone": proj_alone,
+        "verify_with_carried_q_stats": carried_q,
         # MFMA busy share and bf16 flops from rocprofv3 counters (profiles/), when they were
         # taken on the current projection sources
         "proj_mfma_counters": read_mfma(os.path.join(ROOT, "profiles", f"isd_step_{scfg.name}_mfma.txt"),
@@ -514,6 +516,7 @@ def closed_loop(args):
     tpf = st["tpf_meas"]
     print(json.dumps({
         "closed_loop": "isd_qwen3_8b_b64_n4", "steps": steps, "data": "synthetic",
+        "q_stats_carried": bool(cfg.carry_q_stats),
         "graph_ms_per_step": round(1e3 * el / steps, 4), "eager_ms_per_step": round(eager_ms, 4),
         "hot_path_us": {"gated_lora_proj": round(proj_us, 2), "attention": round(att_us, 2),
                         "verify": round(ver_us, 2), "commit": round(commit_us, 2), "total": round(hot_us, 2)},
@@ -662,6 +665,46 @@ def lm_head_bench(args):
 
 # ---------------------------------------------------------------- helpers of the main bench
 PROJ_SETS = 12   # rotated activation + weight sets for the cold projection timing
+
+
+def verify_carried(vsets, vouts, N, dev, reps=30):
+    """Verification of the same input sets with the draft rows' statistics carried from
+    the previous step (isd_verify_carry), as a decoding loop runs it: the statistics come
+    from a real call on a previous step whose rows N..2N-2 are this set's draft rows, made
+    before the timing; the timed calls also hand their own on.  Eager calls with events on
+    the launch stream.  Context beside the main line, which reduces every row itself."""
+    import torch
+    from strided_verify_propose_amd import isd
+    B, R, V = vsets[0]["logits"].shape
+    nb = isd.verify_carry_bytes(B, N, V)
+    if nb == 0 or vsets[0]["draft_logits"] is None:
+        return None
+    carried, nxt = [], torch.empty(nb, dtype=torch.uint8, device=dev)
+    for vs in vsets:
+        prev = vs["logits"].clone()
+        prev[:, N:] = vs["draft_logits"]
+        q = torch.empty(nb, dtype=torch.uint8, device=dev)
+        isd.verify(prev, vs["draft_logits"], vs["draft_ids"], vs["uniforms"], with_diagnostics=False,
+                   q_stats_next=q)
+        carried.append(q)
+        del prev
+    outs = [None] * len(vsets)
+    for k, vs in enumerate(vsets):   # warm-up, and the outputs to compare
+        outs[k] = isd.verify(vs["logits"], vs["draft_logits"], vs["draft_ids"], vs["uniforms"],
+                             with_diagnostics=False, q_stats_prev=carried[k], q_stats_next=nxt)
+    torch.cuda.synchronize()
+    same = all(torch.equal(outs[k][n], vouts[k][n]) for k in range(len(vsets)) for n in vouts[k])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        k = i % len(vsets)
+        vs = vsets[k]
+        e0.record()
+        isd.verify(vs["logits"], vs["draft_logits"], vs["draft_ids"], vs["uniforms"], with_diagnostics=False,
+                   out=outs[k], q_stats_prev=carried[k], q_stats_next=nxt)
+        e1.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+    return {"verify_us": round(us, 2), "outputs_identical_to_verify": bool(same), "calls": reps}
 
 
 def projection_alone(P, packed, pcfg, m_g, dev, reps=48):

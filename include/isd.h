@@ -160,6 +160,31 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
                       float* p_draft, float* q_draft, float* row_lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- verification across steps
+ * A decoding loop's step t+1 verifies drafts drawn from step t's proposal rows N..2N-2
+ * (「I-DLM – introspektive Diffusion Language Models」 "Inference & ISD": the forward that
+ * proposes is the one whose q the next forward's verification uses).  Step t already
+ * reduced those rows to their softmax statistics in order to sample the drafts, so step
+ * t+1 need not reduce its draft_logits again.  isd_verify_carry is isd_verify with two
+ * more buffers, and the same outputs bit for bit:
+ *   q_stats_next  out, may be NULL: this call's statistics of rows N..2N-2 of logits
+ *   q_stats_prev  in, may be NULL (then draft_logits rows are reduced here, as in
+ *                 isd_verify): q_stats_next of the previous call, made with the same B, N,
+ *                 V and temperature, on logits whose rows N..2N-2 are this call's
+ *                 draft_logits rows 0..N-2, bit for bit.  draft_logits is still read for
+ *                 the residual of rejecting requests.  Cold requests ignore it.
+ * Each buffer holds isd_verify_carry_bytes(B, N, V) bytes (0 when N == 1: nothing to
+ * carry); its layout is the library's.  The two must be distinct buffers.  q_stats_prev
+ * requires draft_logits (sampled drafts) and N >= 2; q_stats_next requires N >= 2.
+ * Workspace: isd_verify_workspace_bytes(B, N, V). */
+size_t isd_verify_carry_bytes(int B, int N, int V);
+isd_status isd_verify_carry(isd_dtype dt, const void* logits, const void* draft_logits,
+                            const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                            float temperature, int32_t* n_accept, uint8_t* accept,
+                            int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                            float* p_draft, float* q_draft, float* row_lse, const void* q_stats_prev,
+                            void* q_stats_next, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- verification, no workspace
  * For callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation.  isd_verify with the same arguments

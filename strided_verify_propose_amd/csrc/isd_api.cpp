@@ -87,6 +87,23 @@ isd_status isd_verify(isd_dtype dt, const void* logits, const void* draft_logits
   return hip_status(isd::launch_verify(v, as_stream(stream)), "verify launch");
 }
 
+size_t isd_verify_carry_bytes(int B, int N, int V) { return isd::verify_carry_bytes(B, N, V); }
+
+isd_status isd_verify_carry(isd_dtype dt, const void* logits, const void* draft_logits,
+                            const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                            float temperature, int32_t* n_accept, uint8_t* accept, int32_t* next_token,
+                            int32_t* argmax_ids, int32_t* sampled_ids, float* p_draft, float* q_draft,
+                            float* row_lse, const void* q_stats_prev, void* q_stats_next, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  isd::VerifyLaunch v;
+  const isd_status st = isd::prepare_verify_carry(dt, logits, draft_logits, draft_ids, uniforms, B, N, V,
+                                                  temperature, n_accept, accept, next_token, argmax_ids,
+                                                  sampled_ids, p_draft, q_draft, row_lse, q_stats_prev,
+                                                  q_stats_next, workspace, workspace_bytes, &v);
+  if (st != ISD_OK) return st;
+  return hip_status(isd::launch_verify(v, as_stream(stream)), "verify_carry launch");
+}
+
 // ---------------------------------------------------------------- commit
 isd_status isd_commit(const int32_t* n_accept, const int32_t* next_token, const int32_t* sampled_ids,
                       int32_t* draft_ids, int32_t* ctx_lens, int32_t* tokens, int32_t* counts, int B, int N,

@@ -170,6 +170,12 @@ size_t verify_workspace_bytes(int B, int N, int V) {
   return ver_ws(B, N, V).total;
 }
 
+size_t verify_carry_bytes(int B, int N, int V) {
+  if (B < 1 || B > 65535 || N < 2 || N > 8 || V < 2 || V > (1 << 20)) return 0;
+  const VerWs w = ver_ws(B, N, V);
+  return (size_t)B * (N - 1) * (2 * (size_t)w.SV + w.NSUB) * sizeof(float);
+}
+
 size_t lm_head_verify_workspace_bytes(int B, int N, int V) {
   if (B < 1 || B > 65535 || N < 1 || N > 8 || V < 8 || V > (1 << 20)) return 0;
   return lmh_ws(B, N, V).total;
@@ -321,7 +327,30 @@ isd_status prepare_verify(isd_dtype dt, const void* logits, const void* draft_lo
   v->n_accept = n_accept; v->accept = accept; v->next_token = next_token;
   v->argmax_ids = argmax_ids; v->sampled_ids = sampled_ids;
   v->p_draft = p_draft; v->q_draft = q_draft; v->row_lse = row_lse;
+  v->QS = 2 * w.SV + w.NSUB;
   carve_verify(w, workspace, v);
+  return clear_error();
+}
+
+isd_status prepare_verify_carry(isd_dtype dt, const void* logits, const void* draft_logits,
+                                const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                                float temperature, int32_t* n_accept, uint8_t* accept,
+                                int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                                float* p_draft, float* q_draft, float* row_lse, const void* q_stats_prev,
+                                void* q_stats_next, void* workspace, size_t workspace_bytes, VerifyLaunch* v) {
+  const isd_status st = prepare_verify(dt, logits, draft_logits, draft_ids, uniforms, B, N, V, temperature,
+                                       n_accept, accept, next_token, argmax_ids, sampled_ids, p_draft, q_draft,
+                                       row_lse, workspace, workspace_bytes, v);
+  if (st != ISD_OK) return st;
+  if (N < 2 && (q_stats_prev || q_stats_next))
+    return set_error(ISD_ERR_INVALID_ARG, "verify_carry: N=1 has no draft rows to carry statistics for");
+  if (q_stats_prev && !draft_logits)
+    return set_error(ISD_ERR_INVALID_ARG, "verify_carry: carried statistics need draft_logits (sampled drafts)");
+  if (q_stats_prev && q_stats_prev == q_stats_next)
+    return set_error(ISD_ERR_INVALID_ARG, "verify_carry: q_stats_prev and q_stats_next must be distinct buffers");
+  v->qprev = static_cast<const float*>(q_stats_prev);
+  v->qnext = static_cast<float*>(q_stats_next);
+  if (v->qprev) v->snrow = v->R;  // the draft rows' records come from the previous step
   return clear_error();
 }
 

@@ -86,6 +86,13 @@ struct VerifyLaunch {
   float* csub;                  // [B][RR][NSUB] sum 2^(l c2 - K) per sub-chunk
   WalkState* ws;                // [B]
   float* rsub;                  // [B][NSUB] residual mass per sub-chunk
+  // Statistics carried between the steps of a decoding loop: a step's draft rows are the
+  // previous step's proposal rows N .. 2N-2, whose records that step already computed.
+  // Per request and carried row i < N-1: [SV] chunk max, [SV] chunk reference, [NSUB]
+  // sub-chunk sums (QS floats).
+  const float* qprev;           // this call's draft rows' records, or null (computed here)
+  float* qnext;                 // receives this call's rows N .. 2N-2, or null
+  int QS;                       // floats per carried row: 2 SV + NSUB
 };
 
 // ---------------------------------------------------------------- LM head

@@ -22,6 +22,7 @@ const char* last_error();
 size_t attention_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_ctx_len);
 size_t verify_workspace_bytes(int B, int N, int V);
 size_t lm_head_verify_workspace_bytes(int B, int N, int V);
+size_t verify_carry_bytes(int B, int N, int V);
 size_t proj_workspace_bytes(int M, int K, int Nout, int r);
 size_t proj_packed_bytes(int K, int Nout, int r);
 
@@ -48,6 +49,13 @@ isd_status prepare_verify(isd_dtype dt, const void* logits, const void* draft_lo
                           int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
                           float* p_draft, float* q_draft, float* row_lse, void* workspace,
                           size_t workspace_bytes, VerifyLaunch* v);
+
+isd_status prepare_verify_carry(isd_dtype dt, const void* logits, const void* draft_logits,
+                                const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
+                                float temperature, int32_t* n_accept, uint8_t* accept,
+                                int32_t* next_token, int32_t* argmax_ids, int32_t* sampled_ids,
+                                float* p_draft, float* q_draft, float* row_lse, const void* q_stats_prev,
+                                void* q_stats_next, void* workspace, size_t workspace_bytes, VerifyLaunch* v);
 
 isd_status prepare_commit(const int32_t* n_accept, const int32_t* next_token,
                           const int32_t* sampled_ids, int32_t* draft_ids, int32_t* ctx_lens,

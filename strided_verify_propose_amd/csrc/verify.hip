@@ -107,7 +107,7 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int V, int
 // then 16 lanes per sub-chunk add their consecutive share and reduce in their 16-lane group.
 template <typename T, int ROUNDS = kRounds<T>>
 __device__ __forceinline__ void sub_sums(const float (&s)[ROUNDS], float* lds, float* out,
-                                         int chunk, int nsub, int tid) {
+                                         int chunk, int nsub, int tid, float* out2 = nullptr) {
   constexpr int VE = VecOf<T>::n;
   constexpr int TPS = VSUB / VE;              // threads covering one sub-chunk in a round
   constexpr int SPR = THREADS / TPS;          // sub-chunks per round
@@ -124,7 +124,34 @@ __device__ __forceinline__ void sub_sums(const float (&s)[ROUNDS], float* lds, f
   for (int i = 0; i < PER; ++i) v += src[i];
   v = row16_sum(v);
   const int sub = chunk * SUBS + j;
-  if (p == 0 && sub < nsub) out[sub] = v;
+  if (p == 0 && sub < nsub) {
+    out[sub] = v;
+    if (out2) out2[sub] = v;
+  }
+}
+
+// Chunk maxima, chunk references and sub-chunk sums of row rr of request b: the draft rows'
+// come from the previous step when it carried them, every other row's from this call.
+struct RowRecords {
+  const float* cmax;
+  const float* cref;
+  const float* csub;
+};
+
+__device__ __forceinline__ RowRecords row_records(const VerifyLaunch& v, int b, int rr) {
+  if (v.qprev && rr >= v.R) {
+    const float* q = v.qprev + ((size_t)b * (v.N - 1) + (rr - v.R)) * v.QS;
+    return RowRecords{q, q + v.SV, q + 2 * v.SV};
+  }
+  const size_t rowid = (size_t)b * v.RR + rr;
+  return RowRecords{v.cmax + rowid * v.SV, v.cref + rowid * v.SV, v.csub + rowid * v.NSUB};
+}
+
+// Where this call's row rr of request b is also written for the next step, or null: rows
+// N .. 2N-2 (the proposal rows whose samples become the next step's drafts).
+__device__ __forceinline__ float* carried_row(const VerifyLaunch& v, int b, int rr) {
+  if (!v.qnext || rr < v.N || rr >= v.R) return nullptr;
+  return v.qnext + ((size_t)b * (v.N - 1) + (rr - v.N)) * v.QS;
 }
 
 // ---------------------------------------------------------------- stats pass
@@ -170,12 +197,17 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
     s[k] = acc;
   }
   const size_t rowid = (size_t)b * v.RR + rr;
-  sub_sums<T>(s, lds, v.csub + rowid * v.NSUB, chunk, v.NSUB, tid);
+  float* carry = carried_row(v, b, rr);
+  sub_sums<T>(s, lds, v.csub + rowid * v.NSUB, chunk, v.NSUB, tid, carry ? carry + 2 * v.SV : nullptr);
   if (tid == 0) {
     v.cmax[rowid * v.SV + chunk] = M;
     v.cref[rowid * v.SV + chunk] = K;
     v.cidx[rowid * v.SV + chunk] =
         proposal ? min(min(redi[0], redi[1]), min(redi[2], redi[3])) : INT_MAX;
+    if (carry) {
+      carry[chunk] = M;
+      carry[v.SV + chunk] = K;
+    }
   }
 }
 
@@ -220,6 +252,7 @@ __device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, i
   decode_unit(v, unit, b, rr, chunk);
   const int rowid = b * v.RR + rr;
   const int base = chunk * VCHUNK;
+  float* carry = carried_row(v, b, rr);
   float x[NE];
 #pragma unroll
   for (int k = 0; k < kRounds<T>; ++k) {
@@ -284,12 +317,19 @@ __device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, i
     for (int i = 0; i < PER; ++i) vv += src[i];
     vv = row16_sum(vv);
     const int sub = chunk * VCHUNK_SUBS + j;
-    if (p == 0 && sub < v.NSUB) v.csub[(size_t)rowid * v.NSUB + sub] = vv;
+    if (p == 0 && sub < v.NSUB) {
+      v.csub[(size_t)rowid * v.NSUB + sub] = vv;
+      if (carry) carry[2 * v.SV + sub] = vv;
+    }
   }
   if (tid == 0) {
     v.cmax[(size_t)rowid * v.SV + chunk] = M;
     v.cref[(size_t)rowid * v.SV + chunk] = K;
     v.cidx[(size_t)rowid * v.SV + chunk] = proposal ? min(min(redi[0], redi[1]), min(redi[2], redi[3])) : INT_MAX;
+    if (carry) {
+      carry[chunk] = M;
+      carry[v.SV + chunk] = K;
+    }
   }
 }
 
@@ -522,13 +562,14 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     int iv[RPB];
 #pragma unroll
     for (int q = 0; q < RPB; ++q) {
-      const size_t rowid = (size_t)b * RR + min(r0 + q * WAVES, RR - 1);
+      const int rq = min(r0 + q * WAVES, RR - 1);
+      const RowRecords rec = row_records(v, b, rq);
       const int c = min(lane, SV - 1);
-      mv[q] = v.cmax[rowid * SV + c];
-      kv[q] = v.cref[rowid * SV + c];
-      iv[q] = v.cidx[rowid * SV + c];
+      mv[q] = rec.cmax[c];
+      kv[q] = rec.cref[c];
+      iv[q] = v.cidx[((size_t)b * RR + rq) * SV + c];  // used for the proposal rows only
 #pragma unroll
-      for (int t = 0; t < CSL; ++t) cv[q][t] = v.csub[rowid * NSUB + min(t * 64 + lane, NSUB - 1)];
+      for (int t = 0; t < CSL; ++t) cv[q][t] = rec.csub[min(t * 64 + lane, NSUB - 1)];
     }
     __builtin_amdgcn_sched_barrier(0);
     if (gsrc && !gathered) {
@@ -540,7 +581,7 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     for (int q = 0; q < RPB; ++q) {
       const int rr = r0 + q * WAVES;
       if (rr >= RR || (!lead && rr >= N - 1 && rr < R)) continue;
-      const float* cs = v.csub + ((size_t)b * RR + rr) * NSUB;
+      const float* cs = row_records(v, b, rr).csub;
       const float m = (lane < SV) ? mv[q] : -__builtin_inff();
       const float k = (lane < SV) ? kv[q] : -__builtin_inff();
       const float M = wave_max(m);

@@ -25,6 +25,7 @@ EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
            "isd_pack_kv_pages", "isd_unpack_kv_pages",
            "isd_verify_workspace_bytes", "isd_verify", "isd_verify_noalloc",
+           "isd_verify_carry_bytes", "isd_verify_carry",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
            "isd_proj_packed_bytes", "isd_pack_proj_weights", "isd_pack_proj_weights_kn",
            "isd_gated_lora_proj_packed",
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.isd_verify.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 8 + [vp, sz, vp]
     L.isd_verify_noalloc.restype = i32
     L.isd_verify_noalloc.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 8 + [vp]
+    L.isd_verify_carry_bytes.restype = sz
+    L.isd_verify_carry_bytes.argtypes = [i32] * 3
+    L.isd_verify_carry.restype = i32
+    L.isd_verify_carry.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [f32] + [vp] * 10 + [vp, sz, vp]
     L.isd_gated_lora_workspace_bytes.restype = sz
     L.isd_gated_lora_workspace_bytes.argtypes = [i32] * 4
     L.isd_gated_lora_proj.restype = i32
@@ -216,12 +221,20 @@ def unpack_kv_pages(k_cache, v_cache, k_pages=None, v_pages=None):
 
 
 # ----------------------------------------------------------------------------- verification
+def verify_carry_bytes(B: int, N: int, V: int) -> int:
+    """Bytes of one buffer of statistics carried between steps (0 when N == 1)."""
+    return lib().isd_verify_carry_bytes(B, N, V)
+
+
 def verify(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
-           with_diagnostics: bool = True, out: dict | None = None):
+           with_diagnostics: bool = True, out: dict | None = None, q_stats_prev=None, q_stats_next=None):
     """Vocab-wide verification of one ISD step.  logits [B,2N-1,V]; draft_logits [B,N-1,V]
     or None (argmax drafts); draft_ids [B,N-1] int32; uniforms [B,2N-1] float32.
     Returns a dict of device tensors (n_accept, accept, next_token, argmax_ids,
-    sampled_ids, and p_draft, q_draft, row_lse when with_diagnostics)."""
+    sampled_ids, and p_draft, q_draft, row_lse when with_diagnostics).
+    q_stats_next / q_stats_prev (uint8 device tensors of verify_carry_bytes): this call's
+    statistics of rows N..2N-2 for the next step, and the previous step's for this call's
+    draft rows (isd_verify_carry; same outputs as without them)."""
     B, R, V = logits.shape
     if R % 2 == 0:
         raise ValueError("logits must hold 2N-1 rows per request")
@@ -245,11 +258,25 @@ def verify(logits, draft_logits, draft_ids, uniforms, temperature: float = 1.0,
     L = lib()
     nbytes = L.isd_verify_workspace_bytes(B, N, V)
     w = workspace("verify", nbytes, dev, (B, N, V))
-    _check(L.isd_verify(_dt(logits), _ptr(logits), _ptr(draft_logits), _ptr(draft_ids),
-                        _ptr(uniforms), B, N, V, float(temperature), _ptr(out["n_accept"]),
-                        _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
-                        _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
-                        _ptr(out.get("row_lse")), _ptr(w), w.numel(), _stream(dev)))
+    if q_stats_prev is None and q_stats_next is None:
+        _check(L.isd_verify(_dt(logits), _ptr(logits), _ptr(draft_logits), _ptr(draft_ids),
+                            _ptr(uniforms), B, N, V, float(temperature), _ptr(out["n_accept"]),
+                            _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
+                            _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+                            _ptr(out.get("row_lse")), _ptr(w), w.numel(), _stream(dev)))
+        return out
+    cb = L.isd_verify_carry_bytes(B, N, V)
+    for name, t in (("q_stats_prev", q_stats_prev), ("q_stats_next", q_stats_next)):
+        if t is not None:
+            _need(t, name, torch.uint8, device=dev)
+            if t.numel() < cb:
+                raise ValueError(f"{name}: {t.numel()} bytes, need {cb}")
+    _check(L.isd_verify_carry(_dt(logits), _ptr(logits), _ptr(draft_logits), _ptr(draft_ids),
+                              _ptr(uniforms), B, N, V, float(temperature), _ptr(out["n_accept"]),
+                              _ptr(out["accept"]), _ptr(out["next_token"]), _ptr(out["argmax_ids"]),
+                              _ptr(out["sampled_ids"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+                              _ptr(out.get("row_lse")), _ptr(q_stats_prev), _ptr(q_stats_next),
+                              _ptr(w), w.numel(), _stream(dev)))
     return out
 
 

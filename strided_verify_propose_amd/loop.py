@@ -12,7 +12,9 @@ were drawn from (the previous step's [MASK] rows).  One step:
      block's K/V), verification (cold requests: one exact token from row 0)
   3. isd_commit: context lengths grow by the tokens kept, the next drafts are the
      samples of the [MASK] rows when the request stays hot
-  4. the [MASK] rows are kept as the next step's draft rows
+  4. the [MASK] rows are kept as the next step's draft rows, and so are the softmax
+     statistics verification computed for them (isd_verify_carry): the next step's
+     verification reads them instead of reducing its draft rows again
 Only step 1 and the bookkeeping of 4 are torch operations; 2 and 3 are the library's
 kernels.  The synthetic model costs device time of its own, reported apart from the hot
 path.  (The tokens are never embedded: the model ignores them, as its rows are synthetic.)
@@ -42,6 +44,7 @@ class LoopConfig:
     anchor_sd: float = 3.0
     sigma: float = 0.3            # draft row -> verify row noise (acceptance near 0.9)
     proj: tuple = (4096, 4096, 128)   # K, Nout, r of the R-ISD projection (None: skip)
+    carry_q_stats: bool = True    # hand the [MASK] rows' statistics on to the next step
     seed: int = 1500
 
 
@@ -94,6 +97,13 @@ class ClosedLoop:
             self.y = torch.empty((B * R, Nout), dtype=bf, device=dev)
             self.gate = torch.tensor(([0] * (N - 1) + [1] * N) * B, dtype=torch.uint8, device=dev)
         self.hot = torch.zeros(B, dtype=torch.bool, device=dev)
+        # statistics of this step's rows N..2N-2 for the next step, and the previous step's
+        # for this step's draft rows (zeros before the first step, whose requests are all cold)
+        self.q_next = self.q_prev = None
+        if N > 1 and c.carry_q_stats:
+            nb = isd.verify_carry_bytes(B, N, c.V)
+            self.q_next = torch.zeros(nb, dtype=torch.uint8, device=dev)
+            self.q_prev = torch.zeros(nb, dtype=torch.uint8, device=dev)
 
     # ---------------------------------------------------------------- one step
     def model(self):
@@ -124,7 +134,7 @@ class ClosedLoop:
         if ev is not None:
             ev[2].record()
         isd.verify(self.logits, self.draft_rows if N > 1 else None, self.draft_ids, self.uniforms,
-                   with_diagnostics=False, out=self.out)
+                   with_diagnostics=False, out=self.out, q_stats_prev=self.q_prev, q_stats_next=self.q_next)
         if ev is not None:
             ev[3].record()
         isd.commit(self.out["n_accept"], self.out["next_token"], self.out["sampled_ids"], self.draft_ids,
@@ -149,6 +159,8 @@ class ClosedLoop:
         N = self.cfg.N
         if N > 1:
             self.draft_rows.copy_(self.logits[:, N:])
+        if self.q_next is not None:
+            self.q_prev.copy_(self.q_next)
 
     def step(self, ev=None):
         self.model()

@@ -119,6 +119,25 @@ static void verify_cases() {
                        (int32_t*)P, (int32_t*)P, nullptr, nullptr, nullptr, base, verify_workspace_bytes(3, 1, 1000),
                        &v) == ISD_OK);
   CHECK(v.draft == nullptr && v.RR == 1);
+  // statistics carried between steps: the draft rows leave the stats pass, and a carried
+  // row holds 2 SV + NSUB floats
+  char* prev = reinterpret_cast<char*>(0x10000000);
+  char* next = reinterpret_cast<char*>(0x20000000);
+  CHECK(prepare_verify_carry(ISD_BF16, P, P, (const int32_t*)P, (const float*)P, 64, 4, 151936, 1.f, (int32_t*)P,
+                             (uint8_t*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P, nullptr, nullptr, nullptr, prev, next,
+                             base, need, &v) == ISD_OK);
+  CHECK(v.srow0 == 0 && v.snrow == 7 && v.RR == 10 && v.QS == 2 * 10 + 149);
+  CHECK((size_t)64 * 3 * v.QS * 4 == verify_carry_bytes(64, 4, 151936));
+  CHECK(prepare_verify_carry(ISD_BF16, P, P, (const int32_t*)P, (const float*)P, 64, 4, 151936, 1.f, (int32_t*)P,
+                             (uint8_t*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P, nullptr, nullptr, nullptr, nullptr,
+                             next, base, need, &v) == ISD_OK);
+  CHECK(v.snrow == 10 && v.qprev == nullptr);
+  CHECK(prepare_verify_carry(ISD_BF16, P, P, (const int32_t*)P, (const float*)P, 64, 4, 151936, 1.f, (int32_t*)P,
+                             (uint8_t*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P, nullptr, nullptr, nullptr, prev, prev,
+                             base, need, &v) == ISD_ERR_INVALID_ARG);
+  CHECK(prepare_verify_carry(ISD_BF16, P, nullptr, (const int32_t*)P, (const float*)P, 64, 4, 151936, 1.f,
+                             (int32_t*)P, (uint8_t*)P, (int32_t*)P, (int32_t*)P, (int32_t*)P, nullptr, nullptr, nullptr,
+                             prev, next, base, need, &v) == ISD_ERR_INVALID_ARG);
 }
 
 static void proj_and_lm_head_cases() {

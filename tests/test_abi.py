@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -103,6 +103,36 @@ def test_verify_validation(L, kw, status):
 def test_verify_workspace_query(L):
     assert L.isd_verify_workspace_bytes(64, 4, 151936) > 0
     assert L.isd_verify_workspace_bytes(0, 4, 151936) == 0
+
+
+def ver_carry(L, prev, nxt, **kw):
+    a = dict(dt=1, B=4, N=4, V=151936, T=1.0, ws=FAKE, wsb=1 << 30, draft=FAKE, ids=FAKE, acc=FAKE)
+    a.update(kw)
+    return L.isd_verify_carry(a["dt"], FAKE, a["draft"], a["ids"], FAKE, a["B"], a["N"], a["V"],
+                              ctypes.c_float(a["T"]), FAKE, a["acc"], FAKE, FAKE, FAKE, None, None,
+                              None, prev, nxt, a["ws"], a["wsb"], None)
+
+
+OTHER = ctypes.c_void_p(0x2000)
+
+
+@pytest.mark.parametrize("prev,nxt,kw,status", [
+    (FAKE, FAKE, {}, INVALID),                      # one buffer for both
+    (FAKE, None, dict(draft=None), INVALID),        # carried draft statistics with argmax drafts
+    (None, FAKE, dict(N=1, ids=None, acc=None), INVALID),  # N = 1 has nothing to carry
+    (FAKE, OTHER, dict(wsb=16), WORKSPACE),         # isd_verify's own checks still apply
+    (FAKE, OTHER, dict(T=0.0), INVALID),
+])
+def test_verify_carry_validation(L, prev, nxt, kw, status):
+    assert ver_carry(L, prev, nxt, **kw) == status
+
+
+def test_verify_carry_bytes(L):
+    # per request and carried row: SV chunk maxima and references, NSUB sub-chunk sums
+    SV, NSUB = (151936 + 16383) // 16384, (151936 + 1023) // 1024
+    assert L.isd_verify_carry_bytes(64, 4, 151936) == 64 * 3 * (2 * SV + NSUB) * 4
+    assert L.isd_verify_carry_bytes(64, 1, 151936) == 0
+    assert L.isd_verify_carry_bytes(0, 4, 151936) == 0
 
 
 def proj(L, **kw):
