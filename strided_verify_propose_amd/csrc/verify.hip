@@ -25,6 +25,9 @@
 //   locate   one wave per such request: prefix over those sums, re-read one sub-chunk.
 // Argmax drafts need no residual sums: the residual is p with the draft removed, whose
 // sub-chunk sums the stats pass already has.
+// In a decoding loop a step's draft rows are the previous step's proposal rows N..2N-2:
+// the stats pass can hand those rows' records on (qnext), and the next call can take its
+// draft rows' records from them (qprev) instead of reducing draft_logits again.
 #include <limits.h>
 
 #include <atomic>
