@@ -49,3 +49,24 @@ def test_carried_statistics_change_nothing(name, dtype, B, N, V, seed, T):
         assert torch.equal(bits(got[k]), bits(ref[k])), k
     assert torch.equal(handed_on, handed_on_plain)
     print(f"  n_accept mean {ref['n_accept'].float().mean().item():.2f}", flush=True)
+
+
+def test_statistics_handed_on_do_not_depend_on_the_draft_mode():
+    """With argmax drafts there are no draft rows, but a call still hands its rows N..2N-2
+    on; they equal what a sampled-draft call on the same logits hands on."""
+    B, N, V = 8, 4, 12000
+    c = synth.StepConfig("carry_modes", "bf16", B=B, N=N, Hq=1, Hkv=1, D=64, V=V, ctx=("fixed", 0),
+                         anchor_sd=3.0, noise_sd=0.3, seed=41)
+    v = synth.verify_inputs(c)
+    print(f"verify_carry modes B={B} N={N} V={V}", flush=True)
+    logits, draft = to_dev(v.logits), to_dev(v.draft_logits)
+    ids, u = to_dev(v.draft_ids), to_dev(v.uniforms)
+    nbytes = isd.verify_carry_bytes(B, N, V)
+    sampled, argmax = (torch.zeros(nbytes, dtype=torch.uint8, device=logits.device) for _ in range(2))
+    isd.verify(logits, draft, ids, u, q_stats_next=sampled)
+    ref = isd.verify(logits, None, ids, u)
+    got = isd.verify(logits, None, ids, u, q_stats_next=argmax)
+    torch.cuda.synchronize()
+    assert torch.equal(sampled, argmax)
+    for k in ref:
+        assert torch.equal(bits(got[k]), bits(ref[k])), k
