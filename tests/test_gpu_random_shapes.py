@@ -111,3 +111,40 @@ def test_verify_random_shape(case):
                 a, b = a.view(torch.int32), b.view(torch.int32)
             assert torch.equal(a, b), f"carried statistics change {k}"
     print(f"  compared {compared}, excluded {excluded}", flush=True)
+
+
+def proj_cases(n, seed=20261205):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.choice([1, 7, 63, 64, 65, 130, 448, 700]))
+        K = int(64 * rng.integers(1, 33))            # 64 .. 2048
+        Nout = int(128 * rng.integers(1, 9))         # 128 .. 1024
+        r = int(rng.choice([128, 256]))
+        pattern = tuple(int(x) for x in (rng.random(int(rng.integers(1, 9))) < 0.5))
+        cases.append((i, M, K, Nout, r, pattern))
+    return cases
+
+
+@pytest.mark.parametrize("case", proj_cases(12), ids=lambda c: f"p{c[0]}_M{c[1]}_K{c[2]}_N{c[3]}_r{c[4]}")
+def test_projection_random_shape(case):
+    """Gated projection against the oracle; ungated rows equal the base-only call; packed
+    weights (from either orientation) give the row-major result bit for bit."""
+    i, M, K, Nout, r, pattern = case
+    cfg = synth.ProjConfig(f"rand_proj_{i}", B=1, N=1, K=K, Nout=Nout, r=r, x_sd=1.0, w_sd=0.02,
+                           seed=5000 + i, gate_pattern=pattern)
+    p = synth.proj_inputs(cfg, M=M)
+    print(f"random projection {i}: M={M} K={K} Nout={Nout} r={r} gate pattern {pattern}", flush=True)
+    x, w, a, b, gate = (to_dev(t) for t in (p.x, p.w, p.a, p.b, p.gate))
+    y = isd.gated_lora_proj(x, w, a, b, gate)
+    yb = isd.gated_lora_proj(x, w)
+    yp = isd.gated_lora_proj_packed(x, isd.pack_proj_weights(w, a, b), gate)
+    ykn = isd.gated_lora_proj_packed(
+        x, isd.pack_proj_weights_kn(w.t().contiguous(), a.t().contiguous(), b.t().contiguous()), gate)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y) and torch.equal(ykn, y), "packed results differ from row-major"
+    g = p.gate.astype(bool)
+    Y = to_np(y)
+    assert np.array_equal(Y[~g], to_np(yb)[~g]), "ungated rows differ from the base-only call"
+    worst = assert_close(Y, oracle.gated_lora_proj(p.x, p.w, p.a, p.b, p.gate), RTOL["bf16"], "gated projection")
+    print(f"  worst relative error {worst:.3e}", flush=True)
