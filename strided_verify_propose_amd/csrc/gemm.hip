@@ -7,7 +7,8 @@
 //                tiles of W^T give the base product -- written as bf16 for ungated rows
 //                (exactly what a gate-free call writes) and kept in fp32 for gated
 //                rows -- and the tiles of A^T give T = bf16(X A).
-//   lora_kernel  gated rows only: Y = bf16(base + T B) with T B on MFMA (K = r).
+//   lora_kernel  gated rows only: Y = bf16(base + T B) with T B on MFMA (K = r, every
+//                step's loads at once).
 // Tiles: 64 x 128 per workgroup, 4 waves of 32 x 64 (2 x 4 MFMA 16x16x32 blocks), K in
 // steps of 64: three steps of global loads in flight, one step staged in LDS, and the
 // next step's MFMA fragments read from LDS while the current step's MFMAs run.  Workgroups are
@@ -198,6 +199,40 @@ __global__ __launch_bounds__(THREADS) void base_kernel(const ProjLaunch p) {
     }
 }
 
+// acc as gemm_tile computes it, for a short K = S BK (the delta's K = r): every step's
+// loads go out at once, each step has its own LDS buffer, and one barrier separates the
+// staging from the MFMAs, which run in the same order as in gemm_tile.  With the ring,
+// K = r spent most of its time in the ring's refills past the last step.
+template <int S>
+__device__ void gemm_tile_short(Tiles (&lds)[S], const uint16_t* __restrict__ X, int ldx, int mrows,
+                                const uint16_t* __restrict__ Wt, int ldw, int tid, int wm, int wn, int lane,
+                                f32x4 (&acc)[2][4]) {
+  const uint16_t* pa[A_LOADS];
+  const uint16_t* pb[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i)
+    pa[i] = X + (size_t)min((tid >> 3) + 32 * i, mrows - 1) * ldx + (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) pb[i] = Wt + (size_t)((tid >> 3) + 32 * i) * ldw + (tid & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Stage r[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) issue(r[s], pa, pb, s * BK);
+#pragma unroll
+  for (int s = 0; s < S; ++s) put(lds[s], r[s], tid);
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    Frags f;
+    fetch_frags(f, lds[s], wm, wn, lane);
+    mma(f, acc);
+  }
+}
+
+template <int S>
 __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
   const int mt = (p.M + BM - 1) / BM, nt = p.Nout / BN;
   int tm, tn;
@@ -222,10 +257,9 @@ __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) yb[i][j][e] = p.Ybase[(size_t)gr * p.Nout + n0 + wn * 64 + j * 16 + l16];
     }
-  __shared__ Tiles lds[2];
+  __shared__ Tiles lds[S];
   f32x4 acc[2][4];
-  gemm_tile<PROJ_RING>(lds, p.T + (size_t)m0 * p.r, p.r, mrows, p.Bl + (size_t)n0 * p.r, p.r, p.r, tid, wm, wn,
-            lane, acc);
+  gemm_tile_short<S>(lds, p.T + (size_t)m0 * p.r, p.r, mrows, p.Bl + (size_t)n0 * p.r, p.r, tid, wm, wn, lane, acc);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -274,6 +308,14 @@ hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_lora(const ProjLaunch& p, hipStream_t s) {
+  // K = r, one lora_kernel per supported rank (validated: 128 or 256)
+  if (p.r == 2 * BK) lora_kernel<2><<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
+  else if (p.r == 4 * BK) lora_kernel<4><<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_proj(const ProjLaunch& p, hipStream_t s) {
   if (p.big) return launch_proj_big(p, false, s);
   base_kernel<<<grid_of(p.M, (p.Nout + p.r) * p.ksplit), THREADS, 0, s>>>(p);
@@ -281,12 +323,7 @@ hipError_t launch_proj(const ProjLaunch& p, hipStream_t s) {
     const hipError_t e = launch_proj_reduce(p, s);
     if (e != hipSuccess) return e;
   }
-  if (p.gate) lora_kernel<<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
-  return hipGetLastError();
-}
-
-hipError_t launch_lora(const ProjLaunch& p, hipStream_t s) {
-  lora_kernel<<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
+  if (p.gate) return launch_lora(p, s);
   return hipGetLastError();
 }
 
