@@ -194,9 +194,11 @@ __global__ __launch_bounds__(THREADS) void stats_kernel(const VerifyLaunch v) {
   float s[kRounds<T>];
 #pragma unroll
   for (int k = 0; k < kRounds<T>; ++k) {
-    float acc = 0.f;
+    // started from the first weight: 0 + w = w for every weight (never -0), and the
+    // compiler cannot drop an add of +0 itself
+    float acc = rel_weight(x[k * VE], K, v.c2);
 #pragma unroll
-    for (int j = 0; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
+    for (int j = 1; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
     s[k] = acc;
   }
   const size_t rowid = (size_t)b * v.RR + rr;
@@ -302,9 +304,11 @@ __device__ __forceinline__ void stats_of_unit(const VerifyLaunch& v, int unit, i
   float s[kRounds<T>];
 #pragma unroll
   for (int k = 0; k < kRounds<T>; ++k) {
-    float acc = 0.f;
+    // started from the first weight: 0 + w = w for every weight (never -0), and the
+    // compiler cannot drop an add of +0 itself
+    float acc = rel_weight(x[k * VE], K, v.c2);
 #pragma unroll
-    for (int j = 0; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
+    for (int j = 1; j < VE; ++j) acc += rel_weight(x[k * VE + j], K, v.c2);
     s[k] = acc;
   }
   // sub-chunk sums (as sub_sums, with an LDS-only barrier)
