@@ -257,6 +257,7 @@ def main():
     copy_gbps = 2 * 5 * (1 << 29) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
     ceilings = attainable_bandwidth(dev)
+    kv_sweep = kv_read_sweep_rate(A, att, scfg, maxctx, a_us, dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -298,6 +299,7 @@ def main():
                                                 ("verify", ver_ms))},
         "device_copy_GBps": round(copy_gbps, 1),
         "attainable_GBps": ceilings,
+        "kv_read_sweep": kv_sweep,
         "verify_hbm_frac": round(v_bytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "proj_mfma_frac": round(p_flops / (p_us * 1e-6) / 2.5e15, 4),
         "proj_alone": proj_alone,
@@ -757,6 +759,35 @@ def projection_alone(P, packed, pcfg, m_g, dev, reps=48):
             "reference_hipblaslt_base_only_warm_us": round(lib_warm, 2),
             "reference_hipblaslt_base_only_cold_us": round(lib_cold, 2),
             "reference_hipblaslt_mfma_frac_cold": frac(lib_cold, base_flops)}
+
+
+def kv_read_sweep_rate(A, att, scfg, maxctx, a_us, dev, reps=20):
+    """The cached K/V tiles one attention step reads, read by isd_kv_read_sweep (each once,
+    spread evenly over the GPU, nothing computed), timed with events: the rate this GPU
+    reads those bytes at, against the attention step's own rate for the same bytes."""
+    import torch
+    from strided_verify_propose_amd import isd
+
+    pages = (att.ctx_lens.astype(np.int64) + 15) // 16
+    kv_bytes = int(pages.sum()) * scfg.Hkv * 2 * 16 * scfg.D * 2
+    cs = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call():
+        isd.kv_read_sweep(A["k_cache"], A["v_cache"], A["page_table"], A["ctx_lens"], maxctx, checksum=cs)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    return {"us": round(us, 2), "GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1), "kv_bytes": kv_bytes,
+            "attention_kv_GBps": round(kv_bytes / (a_us * 1e-6) / 1e9, 1),
+            "attention_rate_frac_of_sweep": round(us / a_us, 4)}
 
 
 def attainable_bandwidth(dev):

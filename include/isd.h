@@ -119,6 +119,24 @@ isd_status isd_pack_kv_pages(isd_dtype dt, const void* k_pages, const void* v_pa
 isd_status isd_unpack_kv_pages(isd_dtype dt, const void* k_cache, const void* v_cache, void* k_pages,
                                void* v_pages, int num_pages, int Hkv, int D, void* stream);
 
+/* ---------------------------------------------------------------- KV read sweep
+ * The rate reference for isd_attention_step: reads exactly the cached tiles an attention
+ * step reads for the same requests -- pages 0 .. ceil(L_b/16) - 1 of request b, every KV
+ * head, K and V, with L_b = min(max(ctx_lens[b], 0), max_ctx_len) -- once each, spread
+ * evenly over a resident grid, and computes nothing from them (the paged KV cache of
+ * 「首次超越 AR 模型」 "實際部署：SGLang 整合").  Its time is the time this chip takes to read
+ * those bytes in the attention's tile order with no balancing loss.
+ *   k_cache, v_cache  bf16 tile layouts as at isd_attention_step, num_pages x Hkv tiles
+ *   page_table        [B, max_pages_per_seq] int32; ids are clamped into [0, num_pages)
+ *   ctx_lens          [B] int32
+ *   checksum          one uint32 in device memory, XORed with every 32-bit word read:
+ *                     zero it first to obtain the XOR of all the tiles read
+ * B in [1, 2048]; D in {64, 128}; max_ctx_len <= 16 * max_pages_per_seq.  Errors are
+ * returned before any launch. */
+isd_status isd_kv_read_sweep(const void* k_cache, const void* v_cache, const int32_t* page_table,
+                             const int32_t* ctx_lens, int B, int Hkv, int D, int max_pages_per_seq,
+                             int num_pages, int max_ctx_len, uint32_t* checksum, void* stream);
+
 /* ---------------------------------------------------------------- verification
  * Vocab-wide verification of one ISD step.  Follows: proposals at [MASK] positions from
  * q and verification at clean positions against the anchor p with acceptance

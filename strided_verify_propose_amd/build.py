@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libisd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attention.hip", "kv_pages.hip", "verify.hip", "commit.hip", "gemm.hip", "gemm_packed.hip", "gemm_big.hip",
+SOURCES = ["attention.hip", "kv_pages.hip", "read_sweep.hip", "verify.hip", "commit.hip", "gemm.hip", "gemm_packed.hip", "gemm_big.hip",
            "lm_head.hip",
            "scratch.hip", "isd_validate.cpp", "isd_api.cpp"]
 FLAGS = [

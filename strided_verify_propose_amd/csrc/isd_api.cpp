@@ -70,6 +70,16 @@ isd_status isd_unpack_kv_pages(isd_dtype dt, const void* k_cache, const void* v_
   return hip_status(isd::launch_kv_pages(c, as_stream(stream)), "unpack_kv_pages launch");
 }
 
+isd_status isd_kv_read_sweep(const void* k_cache, const void* v_cache, const int32_t* page_table,
+                             const int32_t* ctx_lens, int B, int Hkv, int D, int max_pages_per_seq,
+                             int num_pages, int max_ctx_len, uint32_t* checksum, void* stream) {
+  isd::KvSweepLaunch c;
+  const isd_status st = isd::prepare_kv_sweep(k_cache, v_cache, page_table, ctx_lens, B, Hkv, D, max_pages_per_seq,
+                                              num_pages, max_ctx_len, checksum, &c);
+  if (st != ISD_OK) return st;
+  return hip_status(isd::launch_kv_sweep(c, as_stream(stream)), "kv_read_sweep launch");
+}
+
 // ---------------------------------------------------------------- verification
 size_t isd_verify_workspace_bytes(int B, int N, int V) { return isd::verify_workspace_bytes(B, N, V); }
 

@@ -292,6 +292,34 @@ isd_status prepare_kv_pages(isd_dtype dt, const void* k_src, const void* v_src, 
   return clear_error();
 }
 
+// ---------------------------------------------------------------- KV read sweep
+isd_status prepare_kv_sweep(const void* k_cache, const void* v_cache, const int32_t* page_table,
+                            const int32_t* ctx_lens, int B, int Hkv, int D, int max_pages_per_seq, int num_pages,
+                            int max_ctx_len, uint32_t* checksum, KvSweepLaunch* c) {
+  if (!k_cache || !v_cache || !page_table || !ctx_lens || !checksum)
+    return set_error(ISD_ERR_INVALID_ARG, "kv_read_sweep: null pointer");
+  if (B < 1 || B > ATTN_MAX_B)
+    return set_error(ISD_ERR_INVALID_ARG, "kv_read_sweep: B=%d out of [1, %d]", B, ATTN_MAX_B);
+  if (Hkv < 1 || Hkv > 65535) return set_error(ISD_ERR_INVALID_ARG, "kv_read_sweep: Hkv=%d out of [1, 65535]", Hkv);
+  if (D != 64 && D != 128) return set_error(ISD_ERR_UNSUPPORTED, "kv_read_sweep: D=%d (supported: 64, 128)", D);
+  if (max_pages_per_seq < 1 || num_pages < 1)
+    return set_error(ISD_ERR_INVALID_ARG, "kv_read_sweep: max_pages_per_seq=%d num_pages=%d", max_pages_per_seq,
+                     num_pages);
+  if (max_ctx_len < 0 || (long long)max_ctx_len > (long long)ATTN_PAGE * max_pages_per_seq)
+    return set_error(ISD_ERR_INVALID_ARG, "kv_read_sweep: max_ctx_len=%d exceeds %d pages", max_ctx_len,
+                     max_pages_per_seq);
+  // the flat tile list is indexed in 32 bits
+  const long long tiles = (long long)B * Hkv * ((max_ctx_len + ATTN_PAGE - 1) / ATTN_PAGE);
+  if (tiles > INT_MAX)
+    return set_error(ISD_ERR_UNSUPPORTED, "kv_read_sweep: %lld tiles exceed 2^31 - 1 per call", tiles);
+  *c = KvSweepLaunch{};
+  c->k_cache = k_cache; c->v_cache = v_cache; c->page_table = page_table; c->ctx_lens = ctx_lens;
+  c->checksum = checksum;
+  c->B = B; c->Hkv = Hkv; c->D = D; c->max_pages = max_pages_per_seq; c->num_pages = num_pages;
+  c->max_ctx_len = max_ctx_len;
+  return clear_error();
+}
+
 // ---------------------------------------------------------------- verification
 isd_status prepare_verify(isd_dtype dt, const void* logits, const void* draft_logits,
                           const int32_t* draft_ids, const float* uniforms, int B, int N, int V,

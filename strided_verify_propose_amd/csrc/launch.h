@@ -11,6 +11,7 @@ namespace isd {
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_kv_pages(const KvPagesLaunch& c, hipStream_t s);
+hipError_t launch_kv_sweep(const KvSweepLaunch& c, hipStream_t s);
 hipError_t launch_verify(const VerifyLaunch& v, hipStream_t s);        // stats + tail
 hipError_t launch_verify_stats(const VerifyLaunch& v, hipStream_t s);  // the stats pass alone
 hipError_t launch_verify_tail(const VerifyLaunch& v, hipStream_t s);   // walk, residual, draws

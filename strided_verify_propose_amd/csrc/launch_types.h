@@ -47,6 +47,16 @@ struct KvPagesLaunch {
   int num_pages, Hkv, D;
 };
 
+// ---------------------------------------------------------------- KV read sweep
+struct KvSweepLaunch {
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* page_table;   // [B][max_pages]
+  const int32_t* ctx_lens;     // [B]
+  uint32_t* checksum;          // one word, XORed with every word read
+  int B, Hkv, D, max_pages, num_pages, max_ctx_len;
+};
+
 // ---------------------------------------------------------------- verification
 constexpr int VCHUNK = 16384;   // vocab entries per stats workgroup
 constexpr int VSUB = 1024;      // vocab entries per sub-chunk (prefix granularity)

@@ -43,6 +43,10 @@ isd_status prepare_attention(isd_dtype dt, const void* q, const void* k_new, con
 isd_status prepare_kv_pages(isd_dtype dt, const void* k_src, const void* v_src, void* k_dst, void* v_dst,
                             int num_pages, int Hkv, int D, int to_tiles, KvPagesLaunch* c);
 
+isd_status prepare_kv_sweep(const void* k_cache, const void* v_cache, const int32_t* page_table,
+                            const int32_t* ctx_lens, int B, int Hkv, int D, int max_pages_per_seq, int num_pages,
+                            int max_ctx_len, uint32_t* checksum, KvSweepLaunch* c);
+
 isd_status prepare_verify(isd_dtype dt, const void* logits, const void* draft_logits,
                           const int32_t* draft_ids, const float* uniforms, int B, int N, int V,
                           float temperature, int32_t* n_accept, uint8_t* accept,

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 EXPORTS = ("isd_abi_version", "isd_status_string", "isd_last_error",
            "isd_attention_workspace_bytes", "isd_attention_step",
-           "isd_pack_kv_pages", "isd_unpack_kv_pages",
+           "isd_pack_kv_pages", "isd_unpack_kv_pages", "isd_kv_read_sweep",
            "isd_verify_workspace_bytes", "isd_verify", "isd_verify_noalloc",
            "isd_verify_carry_bytes", "isd_verify_carry",
            "isd_gated_lora_workspace_bytes", "isd_gated_lora_proj",
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.isd_pack_kv_pages.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [vp]
     L.isd_unpack_kv_pages.restype = i32
     L.isd_unpack_kv_pages.argtypes = [i32] + [vp] * 4 + [i32] * 3 + [vp]
+    L.isd_kv_read_sweep.restype = i32
+    L.isd_kv_read_sweep.argtypes = [vp] * 4 + [i32] * 6 + [vp, vp]
     L.isd_verify_workspace_bytes.restype = sz
     L.isd_verify_workspace_bytes.argtypes = [i32] * 3
     L.isd_verify.restype = i32
@@ -218,6 +220,29 @@ def unpack_kv_pages(k_cache, v_cache, k_pages=None, v_pages=None):
     _check(lib().isd_unpack_kv_pages(_dt(k_cache), _ptr(k_cache), _ptr(v_cache), _ptr(k_pages), _ptr(v_pages),
                                      P, Hkv, D, _stream(dev)))
     return k_pages, v_pages
+
+
+def kv_read_sweep(k_cache, v_cache, page_table, ctx_lens, max_ctx_len: int, checksum=None):
+    """Read the cached K/V tiles an attention step reads for these requests, once each and
+    evenly spread over the GPU, computing nothing from them: the rate reference for
+    attention_step.  checksum (one uint32 word on the device, as an int32 tensor of shape
+    [1]) is XORed with every 32-bit word read; a new one starts at zero.  Returns it."""
+    P, Hkv = k_cache.shape[:2]
+    D = k_cache.shape[2] * 8
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, (P, Hkv, D // 8, PAGE_SIZE, 8), dev)
+    _need(v_cache, "v_cache", torch.bfloat16, (P, Hkv, D // 16, 4, PAGE_SIZE, 4), dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    if page_table.dim() != 2:
+        raise ValueError(f"page_table: shape {tuple(page_table.shape)}, expected (B, max_pages)")
+    B = page_table.shape[0]
+    _need(ctx_lens, "ctx_lens", torch.int32, (B,), dev)
+    if checksum is None:
+        checksum = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(checksum, "checksum", torch.int32, (1,), dev)
+    _check(lib().isd_kv_read_sweep(_ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(ctx_lens), B, Hkv, D,
+                                   page_table.shape[1], P, int(max_ctx_len), _ptr(checksum), _stream(dev)))
+    return checksum
 
 
 # ----------------------------------------------------------------------------- verification

@@ -36,6 +36,10 @@ int main(void) {
         ISD_ERR_UNSUPPORTED);
   CHECK(isd_unpack_kv_pages(ISD_BF16, NULL, fake, (void*)0x3000, (void*)0x4000, 10, 8, 128, NULL) ==
         ISD_ERR_INVALID_ARG);
+  CHECK(isd_kv_read_sweep(fake, fake, (const int32_t*)fake, (const int32_t*)fake, 64, 8, 96, 257, 20000, 4096,
+                          (uint32_t*)fake, NULL) == ISD_ERR_UNSUPPORTED);
+  CHECK(isd_kv_read_sweep(fake, fake, (const int32_t*)fake, (const int32_t*)fake, 64, 8, 128, 257, 20000, 4096,
+                          NULL, NULL) == ISD_ERR_INVALID_ARG);
   CHECK(isd_verify_carry_bytes(64, 4, 151936) > 0 && isd_verify_carry_bytes(64, 1, 151936) == 0);
   CHECK(isd_verify_carry(ISD_BF16, fake, fake, (const int32_t*)fake, (const float*)fake, 4, 4, 151936, 1.f,
                          (int32_t*)fake, (uint8_t*)fake, (int32_t*)fake, (int32_t*)fake, (int32_t*)fake, NULL, NULL,

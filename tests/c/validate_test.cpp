@@ -86,6 +86,20 @@ static void kv_pages_cases() {
   CHECK(prepare_kv_pages(ISD_BF16, k, v, kc, vc, 1000, 8, 80, 1, &c) == ISD_ERR_UNSUPPORTED);
   CHECK(prepare_kv_pages(ISD_BF16, k, v, kc, vc, INT_MAX, 65535, 128, 1, &c) == ISD_ERR_UNSUPPORTED);
   CHECK(prepare_kv_pages(ISD_BF16, k, nullptr, kc, vc, 10, 8, 128, 1, &c) == ISD_ERR_INVALID_ARG);
+
+  KvSweepLaunch s{};
+  const int32_t* pt = reinterpret_cast<const int32_t*>(0x5000);
+  const int32_t* cl = reinterpret_cast<const int32_t*>(0x6000);
+  uint32_t* cs = reinterpret_cast<uint32_t*>(0x7000);
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 64, 8, 128, 257, 20000, 4096, cs, &s) == ISD_OK && s.B == 64 &&
+        s.max_pages == 257 && s.checksum == cs);
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 64, 8, 128, 256, 20000, 4096, cs, &s) == ISD_OK);   // exactly full
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 64, 8, 128, 256, 20000, 4097, cs, &s) == ISD_ERR_INVALID_ARG);
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 2049, 8, 128, 257, 20000, 4096, cs, &s) == ISD_ERR_INVALID_ARG);
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 64, 8, 80, 257, 20000, 4096, cs, &s) == ISD_ERR_UNSUPPORTED);
+  CHECK(prepare_kv_sweep(kc, vc, pt, nullptr, 64, 8, 128, 257, 20000, 4096, cs, &s) == ISD_ERR_INVALID_ARG);
+  CHECK(prepare_kv_sweep(kc, vc, pt, cl, 2048, 65535, 128, 1 << 20, 1 << 30, 1 << 24, cs, &s) ==
+        ISD_ERR_UNSUPPORTED);
 }
 
 static void verify_cases() {
@@ -215,6 +229,11 @@ static void fuzz(int iters) {
       KvPagesLaunch c{};
       (void)prepare_kv_pages(ISD_BF16, P, reinterpret_cast<void*>(0x200000), reinterpret_cast<void*>(0x300000),
                              reinterpret_cast<void*>(0x400000), a0, a1, a2, it & 1, &c);
+    }
+    {
+      KvSweepLaunch c{};
+      (void)prepare_kv_sweep(P, P, (const int32_t*)P, (const int32_t*)P, a0, a1, it & 1 ? 128 : 64, a2, a0, a1,
+                             (uint32_t*)P, &c);
     }
     {
       const size_t need = verify_workspace_bytes(a0, a1, a2);

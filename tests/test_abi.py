@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     assert sorted(isd.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -279,4 +279,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_kv_pages_validation(L, args, status):
     assert L.isd_pack_kv_pages(*args, None) == status
     assert L.isd_unpack_kv_pages(*args, None) == status
+    assert L.isd_last_error() != b""
+
+
+_K, _V, _PT, _CL, _CS = (ctypes.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, _V, _PT, _CL, 64, 8, 128, 257, 20000, 4096, _CS), INVALID),       # null k_cache
+    ((_K, _V, _PT, _CL, 64, 8, 128, 257, 20000, 4096, None), INVALID),        # null checksum
+    ((_K, _V, _PT, _CL, 0, 8, 128, 257, 20000, 4096, _CS), INVALID),          # B = 0
+    ((_K, _V, _PT, _CL, 2049, 8, 128, 257, 20000, 4096, _CS), INVALID),       # B past the bf16 limit
+    ((_K, _V, _PT, _CL, 64, 0, 128, 257, 20000, 4096, _CS), INVALID),         # Hkv = 0
+    ((_K, _V, _PT, _CL, 64, 8, 96, 257, 20000, 4096, _CS), UNSUPPORTED),      # D
+    ((_K, _V, _PT, _CL, 64, 8, 128, 0, 20000, 4096, _CS), INVALID),           # no pages per request
+    ((_K, _V, _PT, _CL, 64, 8, 128, 256, 20000, 4097, _CS), INVALID),         # max_ctx_len past the table
+    ((_K, _V, _PT, _CL, 2048, 65535, 128, 1 << 20, 1 << 30, 1 << 24, _CS), UNSUPPORTED),  # tiles past 2^31 - 1
+])
+def test_kv_read_sweep_validation(L, args, status):
+    """Argument errors of the read sweep come back before anything is launched."""
+    assert L.isd_kv_read_sweep(*args, None) == status
     assert L.isd_last_error() != b""
