@@ -785,9 +785,35 @@ def kv_read_sweep_rate(A, att, scfg, maxctx, a_us, dev, reps=20):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
+
+    # the same kernel over one request whose pages are consecutive (identity page table,
+    # one head): a streaming read of two contiguous 96 MiB buffers, the verification
+    # pass's volume, as that pass's ceiling
+    pages = (96 << 20) // 4096
+    ks = torch.zeros((pages, 1, 16, 16, 8), dtype=torch.bfloat16, device=dev)
+    vs = torch.zeros((pages, 1, 8, 4, 16, 4), dtype=torch.bfloat16, device=dev)
+    ident = torch.arange(pages, dtype=torch.int32, device=dev).reshape(1, pages)
+    lens = torch.full((1,), pages * 16, dtype=torch.int32, device=dev)
+
+    def stream():
+        isd.kv_read_sweep(ks, vs, ident, lens, pages * 16, checksum=cs)
+
+    for _ in range(3):
+        stream()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        stream()
+    e1.record()
+    torch.cuda.synchronize()
+    s_us = e0.elapsed_time(e1) / reps * 1e3
+    s_bytes = 2 * pages * 4096
+    del ks, vs
     return {"us": round(us, 2), "GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1), "kv_bytes": kv_bytes,
             "attention_kv_GBps": round(kv_bytes / (a_us * 1e-6) / 1e9, 1),
-            "attention_rate_frac_of_sweep": round(us / a_us, 4)}
+            "attention_rate_frac_of_sweep": round(us / a_us, 4),
+            "contiguous": {"us": round(s_us, 2), "bytes": s_bytes,
+                           "GBps": round(s_bytes / (s_us * 1e-6) / 1e9, 1)}}
 
 
 def attainable_bandwidth(dev):
