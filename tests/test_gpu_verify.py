@@ -61,6 +61,30 @@ def test_verify_parity(c):
     run(c)
 
 
+def test_verify_max_requests():
+    """65535 requests, the most one call takes (the grids' request dimension at its limit):
+    N = 2, V = 300.  Requests are independent, so the oracle runs on a sample of them --
+    both ends of the batch and 240 seeded picks -- and the sampled rows of the outputs
+    must match it."""
+    c = cfg("bf16_b65535", "bf16", 65535, 2, 300, 24, anchor_sd=1.0, noise_sd=0.5)
+    v = synth.verify_inputs(c)
+    print(f"verify case {c.name} B={c.B} N={c.N} V={c.V}", flush=True)
+    out = isd.verify(to_dev(v.logits), to_dev(v.draft_logits), to_dev(v.draft_ids), to_dev(v.uniforms))
+    torch.cuda.synchronize()
+    bs = np.unique(np.concatenate([np.arange(8), np.arange(c.B - 8, c.B),
+                                   np.random.default_rng(24).integers(0, c.B, 240)]))
+    ref = oracle.verify_step(v.logits[bs], v.draft_logits[bs], v.draft_ids[bs], v.uniforms[bs], c.N, 1.0)
+    idx = torch.as_tensor(bs, device=out["n_accept"].device)
+    sub = {k: t[idx] for k, t in out.items()}
+    compared, excluded = verify_parity(sub, ref, c.N)
+    rt = RTOL[c.dtype]
+    assert_close(to_np(sub["p_draft"]), ref["p_draft"], rt, "p_draft")
+    assert_close(to_np(sub["q_draft"]), ref["q_draft"], rt, "q_draft")
+    assert_close(to_np(sub["row_lse"]), ref["row_lse"], rt, "row_lse")
+    print(f"  {len(bs)} requests: compared {compared} decisions/ids, excluded {excluded}", flush=True)
+    assert compared >= len(bs)
+
+
 def test_verify_temperature():
     run(cfg("bf16_temp", "bf16", 8, 4, 9000, 21), temperature=0.7)
 
