@@ -286,6 +286,8 @@ def main():
             "vocab": scfg.V, "proj": f"{pcfg.M}x{pcfg.K}->{pcfg.Nout} r{pcfg.r}",
             "proj_weights": "row-major" if packed is None else "packed (MFMA fragment order)",
             "verify_input_sets": len(vsets),
+            "seeds": {"attention": scfg.seed, "verify": [scfg.seed + 100 * k for k in range(len(vsets))],
+                      "proj": pcfg.seed},
         },
         "accepted_tokens_per_s": round(steps_per_s * scfg.B * tpf_hat, 1),
         "hot_tokens_per_step": round(float(np.mean(n_acc + 1)) * scfg.B, 2),
@@ -312,7 +314,8 @@ def main():
                      "kernel": "isd_attention_step (attn_bf16_kernel + attn_combine_kernel)",
                      "achieved": round(a_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": a_bytes},
+                     "alg_bytes_per_launch": a_bytes,
+                     "traffic_ratio": None if traffic is None else round(traffic / a_bytes, 4)},
         "timing": ("hip graph replay of whole steps" if graphs else "eager launches"),
         "eager_ms_per_step": round(1e3 * eager_s, 4),
         "input_generation_s": round(gen_s, 1),
