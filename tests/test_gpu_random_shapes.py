@@ -35,7 +35,7 @@ def attention_cases(n, seed=20261203):
     return cases
 
 
-@pytest.mark.parametrize("case", attention_cases(24), ids=lambda c: f"a{c[0]}_{c[1]}_B{c[2]}_N{c[3]}_G{c[4] // c[5]}_D{c[6]}")
+@pytest.mark.parametrize("case", attention_cases(64), ids=lambda c: f"a{c[0]}_{c[1]}_B{c[2]}_N{c[3]}_G{c[4] // c[5]}_D{c[6]}")
 def test_attention_random_shape(case):
     i, dtype, B, N, Hq, Hkv, D, L = case
     cfg = synth.StepConfig(f"rand_attn_{i}", dtype, B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, V=2, ctx=("fixed", 0),
@@ -74,7 +74,7 @@ def verify_cases(n, seed=20261204):
     return cases
 
 
-@pytest.mark.parametrize("case", verify_cases(20), ids=lambda c: f"v{c[0]}_{c[1]}_B{c[2]}_N{c[3]}_V{c[4]}")
+@pytest.mark.parametrize("case", verify_cases(60), ids=lambda c: f"v{c[0]}_{c[1]}_B{c[2]}_N{c[3]}_V{c[4]}")
 def test_verify_random_shape(case):
     i, dtype, B, N, V, argmax, cold, T, sd = case
     cfg = synth.StepConfig(f"rand_ver_{i}", dtype, B=B, N=N, Hq=1, Hkv=1, D=64, V=V, ctx=("fixed", 0),
@@ -126,7 +126,7 @@ def proj_cases(n, seed=20261205):
     return cases
 
 
-@pytest.mark.parametrize("case", proj_cases(12), ids=lambda c: f"p{c[0]}_M{c[1]}_K{c[2]}_N{c[3]}_r{c[4]}")
+@pytest.mark.parametrize("case", proj_cases(32), ids=lambda c: f"p{c[0]}_M{c[1]}_K{c[2]}_N{c[3]}_r{c[4]}")
 def test_projection_random_shape(case):
     """Gated projection against the oracle; ungated rows equal the base-only call; packed
     weights (from either orientation) give the row-major result bit for bit."""
