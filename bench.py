@@ -40,6 +40,9 @@ def parse():
                     help="run the projection on row-major weights instead of the packed layout")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager steps instead of HIP-graph replays of the same steps")
+    ap.add_argument("--steps-per-graph", type=int, default=0,
+                    help="consecutive steps captured in one HIP graph (default: one per verification "
+                         "input set, so each graph holds every set once); 1 replays one graph per step")
     ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
@@ -187,10 +190,15 @@ def main():
     att_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ver_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
 
-    # ---- timed region: K whole steps.  One HIP graph per verification input set holds a
-    # whole step (the same launches as the eager step), so the steps run back to back
-    # without host launch gaps; --no-graph times the eager steps instead.
+    # ---- timed region: K whole steps, replayed from HIP graphs holding the same launches
+    # as the eager step, so the steps run back to back without host launch gaps;
+    # --no-graph times the eager steps instead.
+    # A graph launch costs the GPU some 20 us between graphs, so G consecutive steps (the
+    # verification sets in turn) go into one graph; the steps past a multiple of G replay
+    # one-step graphs.  Every step runs the same launches either way.
     graphs = []
+    multi = None
+    G = args.steps_per_graph or len(vsets)
     if not args.no_graph:
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -204,16 +212,28 @@ def main():
             with torch.cuda.graph(g):
                 step(k)
             graphs.append(g)
+        if G > 1:
+            multi = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(multi):
+                for k in range(G):
+                    step(k % len(vsets))
+            multi.replay()
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
+    if multi is not None:
+        for _ in range(args.steps // G):
+            multi.replay()
+        for i in range(args.steps % G):
             graphs[i % len(graphs)].replay()
-        else:
-            step(i)
+    else:
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
@@ -316,7 +336,8 @@ def main():
                      "frac": round(a_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": a_bytes,
                      "traffic_ratio": None if traffic is None else round(traffic / a_bytes, 4)},
-        "timing": ("hip graph replay of whole steps" if graphs else "eager launches"),
+        "timing": ((f"hip graph replay of whole steps, {G} per graph" if multi is not None
+                    else "hip graph replay of whole steps, one per graph") if graphs else "eager launches"),
         "eager_ms_per_step": round(1e3 * eager_s, 4),
         "input_generation_s": round(gen_s, 1),
     }
@@ -339,8 +360,9 @@ def sweep(args):
     memory-bound.  Qwen3-8B attention shapes with every context at 2048 tokens, the
     151936-entry vocabulary, the 4096 x 4096 r128 projection on C (2N-1) rows with the
     [MASK] rows gated.  Inputs are drawn on the device (torch generator seeded per point),
-    the verification inputs in four rotated sets; each point times 50 replays of a HIP
-    graph per set after an eager pass that times each call with events."""
+    the verification inputs in four rotated sets; each point times 48 steps replayed from
+    one HIP graph holding the four sets' steps in turn, after an eager pass that times
+    each call with events."""
     import torch
 
     from strided_verify_propose_amd import isd
@@ -424,19 +446,19 @@ def sweep(args):
                 step(k)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        graphs = []
-        for k in range(len(vsets)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        # one graph holds the steps of every verification set in turn (a graph launch
+        # costs the GPU some 20 us, a large share of a step at small C)
+        G = len(vsets)
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi):
+            for k in range(G):
                 step(k)
-            graphs.append(g)
-        steps = 50
-        for g in graphs:
-            g.replay()
+        steps = 12 * G
+        multi.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[i % len(graphs)].replay()
+        for _ in range(steps // G):
+            multi.replay()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         n_acc = np.concatenate([vo["n_accept"].cpu().numpy() for vo in vouts])
@@ -457,9 +479,9 @@ def sweep(args):
             "attention_hbm_frac": round(a_bytes / (us[1] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "verify_hbm_frac": round(v_bytes / (us[2] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "proj_mfma_frac": round(p_flops / (us[0] * 1e-6) / 2.5e15, 4),
-            "timing": "hip graph replay of whole steps; per-call times from an eager pass",
+            "timing": f"hip graph replay of whole steps, {G} per graph; per-call times from an eager pass",
             "data": "synthetic"}), flush=True)
-        del A, vsets, vouts, graphs, x, y, att_out
+        del A, vsets, vouts, multi, x, y, att_out
         torch.cuda.empty_cache()
 
 
