@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -35,14 +36,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--verify-sets", type=int, default=3,
                     help="distinct seeded verification inputs rotated over the steps")
+    ap.add_argument("--proj-sets", type=int, default=12,
+                    help="distinct seeded projection inputs (activations and weights) rotated over "
+                         "the steps, so that every step reads its weights from HBM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--proj-row-major", action="store_true",
                     help="run the projection on row-major weights instead of the packed layout")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager steps instead of HIP-graph replays of the same steps")
     ap.add_argument("--steps-per-graph", type=int, default=0,
-                    help="consecutive steps captured in one HIP graph (default: one per verification "
-                         "input set, so each graph holds every set once); 1 replays one graph per step")
+                    help="consecutive steps captured in one HIP graph (default: the least common "
+                         "multiple of the verification and projection set counts, so each graph holds "
+                         "every set); 1 replays one graph per step")
     ap.add_argument("--workload", choices=["qwen3_8b", "qwen3_32b"], default="qwen3_8b")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
@@ -147,6 +152,23 @@ def main():
     P = dict(x=dt(pin.x), w=dt(pin.w), a=dt(pin.a), b=dt(pin.b), gate=dt(pin.gate))
     # weights are packed once, outside the timed region, as a serving system would at load
     packed = None if args.proj_row_major else isd.pack_proj_weights(P["w"], P["a"], P["b"])
+    # the projection's input sets: the seeded host set first, then sets drawn on the device
+    # with the same shapes and distributions (x ~ N(0, 1); w, a, b ~ N(0, w_sd)).  A step
+    # takes set i mod proj_sets: between two uses of a set the other sets' 480 MB and more
+    # pass through the 256 MB last-level cache, as the other layers' weights do in a model
+    # (the attention pages and the logits are read non-temporally and do not evict them).
+    psets = [dict(x=P["x"], w=P["w"], a=P["a"], b=P["b"], packed=packed)]
+    pg = torch.Generator(device=dev)
+    pg.manual_seed(pcfg.seed + 1)
+    for _ in range(1, max(1, args.proj_sets)):
+        ps = dict(x=torch.randn((pcfg.M, pcfg.K), generator=pg, device=dev).to(torch.bfloat16),
+                  w=(torch.randn((pcfg.Nout, pcfg.K), generator=pg, device=dev) * pcfg.w_sd).to(torch.bfloat16),
+                  a=(torch.randn((pcfg.r, pcfg.K), generator=pg, device=dev) * pcfg.w_sd).to(torch.bfloat16),
+                  b=(torch.randn((pcfg.Nout, pcfg.r), generator=pg, device=dev) * pcfg.w_sd).to(torch.bfloat16))
+        if not args.proj_row_major:
+            ps["packed"] = isd.pack_proj_weights(ps["w"], ps["a"], ps["b"])
+            del ps["w"], ps["a"], ps["b"]
+        psets.append(ps)
     gen_s = time.time() - t0
 
     att_out = torch.empty_like(A["q"])
@@ -156,10 +178,11 @@ def main():
     def step(i, ev=None):
         if ev is not None:
             ev[0].record()
+        ps = psets[i % len(psets)]
         if packed is None:
-            isd.gated_lora_proj(P["x"], P["w"], P["a"], P["b"], P["gate"], out=y)
+            isd.gated_lora_proj(ps["x"], ps["w"], ps["a"], ps["b"], P["gate"], out=y)
         else:
-            isd.gated_lora_proj_packed(P["x"], packed, P["gate"], out=y)
+            isd.gated_lora_proj_packed(ps["x"], ps["packed"], P["gate"], out=y)
         if ev is not None:
             ev[1].record()
         isd.attention_step(A["q"], A["k_new"], A["v_new"], A["k_cache"], A["v_cache"],
@@ -193,21 +216,23 @@ def main():
     # ---- timed region: K whole steps, replayed from HIP graphs holding the same launches
     # as the eager step, so the steps run back to back without host launch gaps;
     # --no-graph times the eager steps instead.
-    # A graph launch costs the GPU some 20 us between graphs, so G consecutive steps (the
-    # verification sets in turn) go into one graph; the steps past a multiple of G replay
-    # one-step graphs.  Every step runs the same launches either way.
+    # A graph launch costs the GPU some 20 us between graphs, so G consecutive steps go into
+    # one graph (by default one period of the input rotation: every verification and every
+    # projection set once); the steps past a multiple of G replay one-step graphs.  Every
+    # step runs the same launches either way.
     graphs = []
     multi = None
-    G = args.steps_per_graph or len(vsets)
+    period = math.lcm(len(vsets), len(psets))
+    G = args.steps_per_graph or period
     if not args.no_graph:
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            for k in range(len(vsets)):
+            for k in range(period):
                 step(k)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        for k in range(len(vsets)):
+        for k in range(period):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(k)
@@ -216,7 +241,7 @@ def main():
             multi = torch.cuda.CUDAGraph()
             with torch.cuda.graph(multi):
                 for k in range(G):
-                    step(k % len(vsets))
+                    step(k)
             multi.replay()
         for g in graphs:
             g.replay()
@@ -306,8 +331,10 @@ def main():
             "vocab": scfg.V, "proj": f"{pcfg.M}x{pcfg.K}->{pcfg.Nout} r{pcfg.r}",
             "proj_weights": "row-major" if packed is None else "packed (MFMA fragment order)",
             "verify_input_sets": len(vsets),
+            "proj_input_sets": len(psets),
             "seeds": {"attention": scfg.seed, "verify": [scfg.seed + 100 * k for k in range(len(vsets))],
-                      "proj": pcfg.seed},
+                      "proj": pcfg.seed,
+                      "proj_device_sets": f"torch.Generator(cuda).manual_seed({pcfg.seed + 1})"},
         },
         "accepted_tokens_per_s": round(steps_per_s * scfg.B * tpf_hat, 1),
         "hot_tokens_per_step": round(float(np.mean(n_acc + 1)) * scfg.B, 2),

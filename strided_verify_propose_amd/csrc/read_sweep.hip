@@ -72,9 +72,9 @@ __global__ __launch_bounds__(64 * WAVES) void kv_sweep_kernel(const KvSweepLaunc
       const int id = min(max(c.page_table[(size_t)b * c.max_pages + j], 0), c.num_pages - 1);
       const size_t o = ((size_t)id * c.Hkv + h) * TILE_U4;
 #pragma unroll
-      for (int q = 0; q < LOADS; ++q) {
-        r[t][q] = k[o + q * 64 + lane];
-        r[t][LOADS + q] = v[o + q * 64 + lane];
+      for (int q = 0; q < LOADS; ++q) {  // non-temporal, as the attention step reads them
+        r[t][q] = __builtin_nontemporal_load(k + o + q * 64 + lane);
+        r[t][LOADS + q] = __builtin_nontemporal_load(v + o + q * 64 + lane);
       }
     }
 #pragma unroll

@@ -242,8 +242,9 @@ __device__ __forceinline__ void load_raw(const VerifyLaunch& v, int unit, int ti
 #pragma unroll
   for (int k = 0; k < kRounds<T>; ++k) {
     const int e0 = base + k * THREADS * VE + tid * VE;
-    // past the row's end: load its first 16 bytes (in bounds), replaced by -inf below
-    r.w[k] = *reinterpret_cast<const u32x4*>(row + (e0 < v.V ? e0 : 0));
+    // past the row's end: load its first 16 bytes (in bounds), replaced by -inf below;
+    // non-temporal: the stats pass reads each logit once
+    r.w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (e0 < v.V ? e0 : 0)));
   }
 }
 
