@@ -387,9 +387,9 @@ def sweep(args):
     memory-bound.  Qwen3-8B attention shapes with every context at 2048 tokens, the
     151936-entry vocabulary, the 4096 x 4096 r128 projection on C (2N-1) rows with the
     [MASK] rows gated.  Inputs are drawn on the device (torch generator seeded per point),
-    the verification inputs in four rotated sets; each point times 48 steps replayed from
-    one HIP graph holding the four sets' steps in turn, after an eager pass that times
-    each call with events."""
+    the verification inputs in four rotated sets and the projection weights in twelve;
+    each point times 48 steps replayed from one HIP graph holding one period of that
+    rotation, after an eager pass that times each call with events."""
     import torch
 
     from strided_verify_propose_amd import isd
@@ -399,11 +399,17 @@ def sweep(args):
     K, Nout, r = 4096, 4096, 128
     gen = torch.Generator(device=dev)
     gen.manual_seed(1300)
-    w = (torch.randn((Nout, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-    a = (torch.randn((r, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-    b = (torch.randn((Nout, r), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-    packed = isd.pack_proj_weights(w, a, b)
-    del w, a, b
+    # PROJ_SETS weight sets rotated over the steps, so that the projection reads its
+    # weights from HBM every step, as in a model whose other layers' weights pass between
+    # two uses (the attention pages and the logits are read non-temporally and would not
+    # evict a single set)
+    packs = []
+    for _ in range(PROJ_SETS):
+        w = (torch.randn((Nout, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        a = (torch.randn((r, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        b = (torch.randn((Nout, r), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        packs.append(isd.pack_proj_weights(w, a, b))
+        del w, a, b
     from strided_verify_propose_amd import synth
     Cs = [int(c) for c in args.sweep_c.split(",")]
     Ns = [int(n) for n in args.sweep_n.split(",")]
@@ -446,7 +452,7 @@ def sweep(args):
         def step(i, ev=None):
             if ev is not None:
                 ev[0].record()
-            isd.gated_lora_proj_packed(x, packed, gate, out=y)
+            isd.gated_lora_proj_packed(x, packs[i % len(packs)], gate, out=y)
             if ev is not None:
                 ev[1].record()
             isd.attention_step(A["q"], A["k_new"], A["v_new"], A["k_cache"], A["v_cache"],
@@ -473,14 +479,15 @@ def sweep(args):
                 step(k)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        # one graph holds the steps of every verification set in turn (a graph launch
-        # costs the GPU some 20 us, a large share of a step at small C)
-        G = len(vsets)
+        # one graph holds one period of the rotation, every verification and projection
+        # set in turn (a graph launch costs the GPU some 20 us, a large share of a step at
+        # small C)
+        G = math.lcm(len(vsets), len(packs))
         multi = torch.cuda.CUDAGraph()
         with torch.cuda.graph(multi):
             for k in range(G):
                 step(k)
-        steps = 12 * G
+        steps = 4 * G
         multi.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
