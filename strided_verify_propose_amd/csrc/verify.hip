@@ -34,6 +34,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "tiles.h"
 
 namespace isd {
 namespace {
@@ -518,11 +519,23 @@ __device__ int sample_row(const VerifyLaunch& v, int b, int rr, const double* fa
 // each); the last workgroup of a request writes the walk's outputs and takes the
 // inverse-CDF draws, and with sampled drafts the others each sum their chunk of the
 // residual max(0, p - q~) of a rejecting request.
+// Workgroups of one request per launch: the residual chunks, then the lead.
+__host__ __device__ inline int walk_groups(const VerifyLaunch& v) {
+  return v.draft ? (v.NSUB + VCHUNK_SUBS / RSPLIT - 1) / (VCHUNK_SUBS / RSPLIT) + 1 : 1;
+}
+
+// One-dimensional grid of XCDS * ceil(B / XCDS) * walk_groups workgroups.  Workgroups are
+// dispatched to the XCDs round-robin by id, so id = x + XCDS * slot runs on XCD x; request b
+// takes XCD b % XCDS and slots (b / XCDS) * groups + chunk there, so all its workgroups share
+// one L2 for the records and the gathers they all read.  Ids past the last request exit.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaunch v) {
   constexpr int WAVES = THREADS / 64;
-  const int chunk = blockIdx.x, b = blockIdx.y;
-  const bool lead = chunk == (int)gridDim.x - 1;
+  const int groups = walk_groups(v);
+  const int slot = (int)blockIdx.x / XCDS;
+  const int chunk = slot % groups, b = (slot / groups) * XCDS + (int)blockIdx.x % XCDS;
+  if (b >= v.B) return;
+  const bool lead = chunk == groups - 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = v.N, R = v.R, RR = v.RR, SV = v.SV, NSUB = v.NSUB;
   const T* lg = static_cast<const T*>(v.logits);
@@ -570,7 +583,11 @@ __global__ __launch_bounds__(THREADS) void walk_residual_kernel(const VerifyLaun
     int iv[RPB];
 #pragma unroll
     for (int q = 0; q < RPB; ++q) {
-      const int rq = min(r0 + q * WAVES, RR - 1);
+      // rows this workgroup skips below (the proposal rows outside the lead workgroup)
+      // load row 0's records again, which the cache already holds: a uniform select,
+      // not a branch, so the compiler's wait counts stay exact
+      const int rr_ = min(r0 + q * WAVES, RR - 1);
+      const int rq = (!lead && rr_ >= N - 1 && rr_ < R) ? 0 : rr_;
       const RowRecords rec = row_records(v, b, rq);
       const int c = min(lane, SV - 1);
       mv[q] = rec.cmax[c];
@@ -847,7 +864,7 @@ hipError_t launch_stats_typed(const VerifyLaunch& v, hipStream_t s) {
 template <typename T>
 hipError_t launch_tail_typed(const VerifyLaunch& v, hipStream_t s) {
   const bool vec = ((size_t)v.V * sizeof(T)) % 16 == 0;
-  const dim3 g2(v.draft ? (v.NSUB + VCHUNK_SUBS / RSPLIT - 1) / (VCHUNK_SUBS / RSPLIT) + 1 : 1, v.B);
+  const unsigned g2 = (unsigned)(XCDS * ((v.B + XCDS - 1) / XCDS) * walk_groups(v));
   if (vec) walk_residual_kernel<T, true><<<g2, THREADS, 0, s>>>(v);
   else walk_residual_kernel<T, false><<<g2, THREADS, 0, s>>>(v);
   if (v.draft) {
