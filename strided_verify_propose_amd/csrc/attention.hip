@@ -224,6 +224,15 @@ __device__ __forceinline__ int holder(int x, int T, int W) {
   return w;
 }
 
+// Share held by the workgroup with id `id` of a grid of W.  Workgroups are dispatched to the
+// XCDs round-robin by id, so with W a multiple of 8 XCD x takes the contiguous shares
+// x W/8 .. (x+1) W/8 - 1: the pieces of an item split between neighbouring shares are then
+// mostly written and merged on one XCD, through one L2.  The combine kernel uses the same
+// map.  Shares, and so results, do not depend on it.
+__device__ __forceinline__ int share_of(int id, int W) {
+  return (W % 8 == 0) ? (id % 8) * (W / 8) + id / 8 : id;
+}
+
 // Record of the split item whose first piece a workgroup holds (at most one: the item its
 // share ends inside), for the merge kernel: request, KV head, start of the item's cost
 // interval, end of its real units, total cost.
@@ -244,7 +253,7 @@ void attn_bf16_kernel(const AttnLaunch a) {
 
   build_prefix(a, pre);
   const int T = pre[a.B];
-  const int W = gridDim.x, w = blockIdx.x;
+  const int W = gridDim.x, w = share_of(blockIdx.x, W);
   const int lo = range_lo(w, T, W), hi = range_lo(w + 1, T, W);
 
   const int R = a.R, G = a.G, Hq = a.Hq, Hkv = a.Hkv, RG = R * G;
@@ -503,7 +512,7 @@ static_assert(COMBINE_THREADS == 4 * 64, "the combine's few-piece path maps thre
 
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(const AttnLaunch a, int W) {
-  const int w0 = blockIdx.x;
+  const int w0 = share_of(blockIdx.x, W);
   const int tid = threadIdx.x;
   const int* rec = a.rec + (size_t)w0 * REC_INTS;
   const int b = rec[0];
