@@ -234,9 +234,12 @@ __device__ void gemm_tile_short(Tiles (&lds)[S], const uint16_t* __restrict__ X,
 
 template <int S>
 __global__ __launch_bounds__(THREADS) void lora_kernel(const ProjLaunch p) {
-  const int mt = (p.M + BM - 1) / BM, nt = p.Nout / BN;
+  // tiles numbered over the base grid's Nout + r columns, so that tile (tm, tn) runs on the
+  // XCD whose base-kernel workgroup wrote its fp32 base product (one L2); the A^T column
+  // tiles have no delta
+  const int mt = (p.M + BM - 1) / BM, ntb = (p.Nout + p.r) / BN;
   int tm, tn;
-  if (!tile_of(blockIdx.x, mt, nt, tm, tn)) return;
+  if (!tile_of(blockIdx.x, mt, ntb, tm, tn) || tn >= p.Nout / BN) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, gq = lane >> 4;
@@ -310,8 +313,8 @@ hipError_t launch_proj_reduce(const ProjLaunch& p, hipStream_t s) {
 
 hipError_t launch_lora(const ProjLaunch& p, hipStream_t s) {
   // K = r, one lora_kernel per supported rank (validated: 128 or 256)
-  if (p.r == 2 * BK) lora_kernel<2><<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
-  else if (p.r == 4 * BK) lora_kernel<4><<<grid_of(p.M, p.Nout), THREADS, 0, s>>>(p);
+  if (p.r == 2 * BK) lora_kernel<2><<<grid_of(p.M, p.Nout + p.r), THREADS, 0, s>>>(p);
+  else if (p.r == 4 * BK) lora_kernel<4><<<grid_of(p.M, p.Nout + p.r), THREADS, 0, s>>>(p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
