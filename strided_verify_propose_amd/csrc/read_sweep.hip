@@ -8,7 +8,7 @@
 // wave g of a grid of G waves takes tiles g, g + G, g + 2G, ...: every wave holds the same
 // number of tiles, so no balancing loss enters the rate.  One workgroup of 8 waves per CU,
 // as the attention kernel runs, with two tiles of loads in flight per wave (one, two or
-// four read at the same rate).
+// four read at the same rate) and the next two tiles' page ids loaded ahead of them.
 #include <atomic>
 
 #include "device.h"
@@ -59,18 +59,37 @@ __global__ __launch_bounds__(64 * WAVES) void kv_sweep_kernel(const KvSweepLaunc
   const int g = blockIdx.x * WAVES + (threadIdx.x >> 6), G = gridDim.x * WAVES;
   const u32x4* __restrict__ k = static_cast<const u32x4*>(c.k_cache);
   const u32x4* __restrict__ v = static_cast<const u32x4*>(c.v_cache);
+  if (total <= 0) return;  // no cached tile (uniform across the workgroup)
   uint32_t x = 0;
-  int b = 0;  // request of the wave's current tile: its tiles ascend, so b only moves on
+  // The page ids of a batch's tiles are loaded one batch ahead, so the tiles' own loads
+  // never wait on a page-table round trip (the attention kernel, too, loads the page ids
+  // of a piece's pages ahead of them).
+  int b = 0;  // request of the look-ahead tiles: they ascend, so b only moves on
+  int idn[NT], hn[NT];
+  auto look = [&](int i0n) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int i = min(i0n + G * t, total - 1);  // past the end: the last tile again, not folded
+      while (pre[b + 1] <= i) ++b;
+      const int n = (pre[b + 1] - pre[b]) / c.Hkv;  // pages of request b (>= 1: it holds tile i)
+      const int rr = i - pre[b], h = rr / n, j = rr - h * n;
+      idn[t] = c.page_table[(size_t)b * c.max_pages + j];
+      hn[t] = h;
+    }
+  };
+  look(g);
   for (int i0 = g; i0 < total; i0 += G * NT) {
+    int id[NT], hh[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      id[t] = min(max(idn[t], 0), c.num_pages - 1);
+      hh[t] = hn[t];
+    }
+    look(i0 + G * NT);
     u32x4 r[NT][2 * LOADS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int i = min(i0 + G * t, total - 1);  // past the end: the last tile again, not folded
-      while (pre[b + 1] <= i) ++b;
-      const int n = (pre[b + 1] - pre[b]) / c.Hkv;  // pages of request b
-      const int rr = i - pre[b], h = rr / n, j = rr - h * n;
-      const int id = min(max(c.page_table[(size_t)b * c.max_pages + j], 0), c.num_pages - 1);
-      const size_t o = ((size_t)id * c.Hkv + h) * TILE_U4;
+      const size_t o = ((size_t)id[t] * c.Hkv + hh[t]) * TILE_U4;
 #pragma unroll
       for (int q = 0; q < LOADS; ++q) {  // non-temporal, as the attention step reads them
         r[t][q] = __builtin_nontemporal_load(k + o + q * 64 + lane);
